@@ -1,0 +1,231 @@
+"""Pins of the oracle's per-vector quantisers and record layout (CPU only)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+H128 = None
+
+
+def _hadamard():
+    global H128
+    if H128 is None:
+        i = np.arange(128)
+        pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+        H128 = np.where(pc % 2 == 1, -1.0, 1.0) / np.sqrt(128.0)
+    return H128
+
+
+def h2f(bits):
+    return float(np.array([bits], np.uint16).view(np.float16)[0])
+
+
+# ------------------------------------------------------------ k3v4_nc keys ---
+
+def test_k3_codes_are_nearest_centroid():
+    """Lloyd-Max coding of the rotated unit vector = nearest centroid, except
+    within rounding distance of a threshold."""
+    c, th = oracle.codebook()
+    rng = np.random.default_rng(21)
+    H = _hadamard()
+    for _ in range(200):
+        k = rng.standard_normal(128).astype(np.float16)
+        codes, nh, gh = oracle.quant_key_k3(k)
+        x = k.astype(np.float64)
+        y = H @ x / np.linalg.norm(x)
+        nearest = np.argmin(np.abs(y[:, None] - c.astype(np.float64)[None, :]), axis=1)
+        close = np.min(np.abs(y[:, None] - th.astype(np.float64)[None, :]), axis=1) < 1e-6
+        assert np.all((codes == nearest) | close)
+        assert abs(h2f(nh) - np.linalg.norm(x)) <= 2.0 ** -11 * np.linalg.norm(x)
+
+
+def test_k3_norm_correction_restores_norm():
+    c, _ = oracle.codebook()
+    rng = np.random.default_rng(22)
+    for _ in range(200):
+        k = (rng.standard_normal(128) * rng.uniform(0.1, 10)).astype(np.float16)
+        codes, nh, gh = oracle.quant_key_k3(k)
+        khat = c[codes].astype(np.float64) * h2f(nh) * h2f(gh)
+        n = np.linalg.norm(k.astype(np.float64))
+        # n and gamma are each rounded to binary16 (2^-11 relative each)
+        assert abs(np.linalg.norm(khat) - n) <= 2.5 * 2.0 ** -11 * n
+
+
+def test_k3_distortion_near_gaussian_model():
+    """Mean squared error of the unit-vector reconstruction (before norm
+    correction) is close to the Gaussian-model Lloyd-Max MSE 0.03454."""
+    c, _ = oracle.codebook()
+    rng = np.random.default_rng(23)
+    H = _hadamard()
+    errs = []
+    for _ in range(3000):
+        k = rng.standard_normal(128).astype(np.float16)
+        codes, _, _ = oracle.quant_key_k3(k)
+        x = k.astype(np.float64)
+        y = H @ x / np.linalg.norm(x)
+        errs.append(np.sum((y - c[codes]) ** 2))
+    assert abs(np.mean(errs) - 0.03454) < 0.002
+
+
+def test_k3_zero_vector():
+    codes, nh, gh = oracle.quant_key_k3(np.zeros(128, np.float16))
+    assert np.all(codes == 0) and nh == 0
+    c, _ = oracle.codebook()
+    assert h2f(gh) == pytest.approx(1 / np.sqrt(128 * c[0].astype(np.float64) ** 2), rel=1e-3)
+
+
+# --------------------------------------------------------------- k8 keys ---
+
+def test_k8_relative_error_and_scale():
+    rng = np.random.default_rng(24)
+    for _ in range(200):
+        k = (rng.standard_normal(128) * rng.uniform(0.01, 50)).astype(np.float16)
+        codes, sh = oracle.quant_key_k8(k)
+        s = h2f(sh)
+        amax = np.max(np.abs(k.astype(np.float64)))
+        assert abs(s - amax / 448) <= 2.0 ** -11 * amax / 448
+        dec = np.array([oracle.e4m3_decode(int(cc)) for cc in codes], np.float64)
+        assert not np.any(np.isnan(dec))
+        kh = dec * s
+        x = k.astype(np.float64)
+        normal = np.abs(x / s) >= 2.0 ** -6
+        # relative half-ulp of a 3-bit mantissa, plus the binary32 division
+        assert np.all(np.abs(kh - x)[normal] <= (2.0 ** -4 + 1e-6) * np.abs(x)[normal])
+        assert np.all(np.abs(kh - x)[~normal] <= 2.0 ** -10 * s * 1.0001)
+        assert np.max(np.abs(dec)) <= 448
+
+
+def test_k8_zero_vector():
+    codes, sh = oracle.quant_key_k8(np.zeros(128, np.float16))
+    assert sh == 0 and np.all(codes == 0)
+
+
+# ---------------------------------------------------------------- values ---
+
+def test_values_error_bound_and_endpoints():
+    rng = np.random.default_rng(25)
+    for _ in range(300):
+        v = (rng.standard_normal(128) * rng.uniform(0.01, 30) + rng.uniform(-5, 5)).astype(np.float16)
+        codes, sh, zh = oracle.quant_val(v)
+        s, z = h2f(sh), h2f(zh)
+        x = v.astype(np.float64)
+        assert z == x.min()
+        vhat = codes * s + z
+        assert np.all(np.abs(vhat - x) <= s / 2 * (1 + 1e-6) + 1e-7 * np.abs(x).max())
+        assert codes[np.argmin(x)] == 0 and codes[np.argmax(x)] == 15
+        assert codes.max() <= 15
+
+
+def test_values_constant_vector_exact():
+    v = np.full(128, 1.5, np.float16)
+    codes, sh, zh = oracle.quant_val(v)
+    assert sh == 0 and np.all(codes == 0) and h2f(zh) == 1.5
+
+
+# ---------------------------------------------------------------- layout ---
+
+def _read_k3_examples():
+    out = []
+    with open(os.path.join(GOLDEN, "k3_pack_worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, nz, exp = line.split()
+            codes = np.zeros(128, np.uint8)
+            for item in nz.split(","):
+                d, cc = item.split(":")
+                codes[int(d)] = int(cc)
+            expected = np.zeros(48, np.uint8)
+            for item in exp.split(","):
+                i, hx = item.split(":")
+                expected[int(i)] = int(hx, 16)
+            out.append((name, codes, expected))
+    return out
+
+
+@pytest.mark.parametrize("example", _read_k3_examples(), ids=lambda e: e[0])
+def test_k3_pack_worked_examples(example):
+    _, codes, expected = example
+    block = np.zeros(oracle.block_bytes(oracle.K3V4_NC), np.uint8)
+    oracle.write_record(oracle.K3V4_NC, block, 0, codes, np.zeros(128, np.uint8), 0, 0, 0, 0)
+    assert np.array_equal(block[:48], expected)
+
+
+def test_value_nibble_worked_examples():
+    rows = []
+    with open(os.path.join(GOLDEN, "value_nibble_worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x, 16) if i == 5 else int(x) for i, x in enumerate(line.split())])
+    for preset, voff in ((oracle.K3V4_NC, 768), (oracle.K8V4, 2048)):
+        for tb, p, lo, hi, off, byte in rows:
+            block = np.zeros(oracle.block_bytes(preset), np.uint8)
+            vc = np.zeros(128, np.uint8)
+            vc[2 * p], vc[2 * p + 1] = lo, hi
+            oracle.write_record(preset, block, tb, np.zeros(128, np.uint8), vc, 0, 0, 0, 0)
+            nz = np.nonzero(block)[0]
+            assert list(nz) == ([voff + off] if byte else [])
+            assert block[voff + off] == byte
+
+
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+def test_record_round_trip_and_slot_size(preset):
+    assert oracle.slot_bytes(preset) == (120 if preset == oracle.K3V4_NC else 198)
+    assert oracle.block_bytes(preset) == 16 * oracle.slot_bytes(preset)
+    rng = np.random.default_rng(26)
+    block = np.zeros(oracle.block_bytes(preset), np.uint8)
+    recs = []
+    for tb in rng.permutation(16):
+        kc = rng.integers(0, 8 if preset == oracle.K3V4_NC else 256, 128).astype(np.uint8)
+        vc = rng.integers(0, 16, 128).astype(np.uint8)
+        m = [int(x) for x in rng.integers(0, 65536, 4)]
+        if preset == oracle.K8V4:
+            m[1] = 0
+        oracle.write_record(preset, block, int(tb), kc, vc, *m)
+        recs.append((int(tb), kc, vc, m))
+    for tb, kc, vc, m in recs:
+        kc2, vc2, *m2 = oracle.read_record(preset, block, tb)
+        assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc) and m2 == m
+    # every byte of the block belongs to exactly one token's record
+    seen = np.zeros(block.size, np.int32)
+    for tb in range(16):
+        b2 = np.zeros_like(block)
+        oracle.write_record(preset, b2, tb, np.full(128, 7 if preset == oracle.K3V4_NC else 255, np.uint8),
+                            np.full(128, 15, np.uint8), 0xFFFF, 0xFFFF if preset == oracle.K3V4_NC else 0,
+                            0xFFFF, 0xFFFF)
+        seen += (b2 != 0)
+    assert np.all(seen == 1)
+
+
+def test_store_writes_the_quantised_record():
+    from tests import synth
+    rng = np.random.default_rng(27)
+    for preset in (oracle.K8V4, oracle.K3V4_NC):
+        B, Hk, S = 2, 2, 40
+        cache = np.zeros(oracle.cache_bytes(preset, B, Hk, S), np.uint8)
+        K = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+        V = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+        si, po = synth.token_lists(B, S)
+        oracle.store(preset, cache, B, Hk, S, synth.rows(K), synth.rows(V), si, po)
+        nblk = (S + 15) // 16
+        bb = oracle.block_bytes(preset)
+        for (b, s, hk) in [(0, 0, 0), (1, 39, 1), (0, 17, 1), (1, 16, 0)]:
+            blk = cache[((b * Hk + hk) * nblk + s // 16) * bb:][:bb]
+            kc, vc, m0, m1, vs, vz = oracle.read_record(preset, blk, s % 16)
+            if preset == oracle.K3V4_NC:
+                c2, n2, g2 = oracle.quant_key_k3(K[b, s, hk])
+                assert (m0, m1) == (n2, g2)
+            else:
+                c2, s2 = oracle.quant_key_k8(K[b, s, hk])
+                assert m0 == s2
+            v2, vs2, vz2 = oracle.quant_val(V[b, s, hk])
+            assert np.array_equal(kc, c2) and np.array_equal(vc, v2) and (vs, vz) == (vs2, vz2)
+        # untouched tail of the last block stays zero
+        with pytest.raises(ValueError):
+            oracle.store(preset, cache, B, Hk, S, synth.rows(K)[:1], synth.rows(V)[:1],
+                         np.array([2], np.int32), np.array([0], np.int32))
