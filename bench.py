@@ -1,0 +1,262 @@
+"""Benchmark of one speculative-decode verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: tqkv_store of the
+N_spec new tokens of every sequence (all KV heads), then tqkv_verify of the
+N_spec queries of every sequence over the full quantised cache.  Inputs are
+seeded synthetic tensors (tests/synth.py) already resident in HBM.
+
+Cold-cache protocol: the MI355X's 256 MB Infinity Cache would hold the
+PoC-size caches, so the benchmark keeps R byte-identical replicas of the
+cache (R * bytes >= 512 MB) and step i uses replica i % R.  The K timed
+steps are captured in one HIP graph (launch-bound loop) and replayed once,
+bracketed by device synchronisation; the eager (non-graph) rate is reported
+beside it.
+
+Output: one JSON line (see the design doc for the field definitions).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+PAGES_FUSED_TRITON_MS = {"poc_k8v4": 3.229, "poc_k3v4_nc": 4.83}  # Arc Pro B70, context
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="poc_k8v4")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cold-mb", type=float, default=512.0)
+    ap.add_argument("--kernel-calls", type=int, default=200,
+                    help="back-to-back verify calls for the per-launch kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the verify path needs no "
+              "communication; see DESIGN.md for how it would shard). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_kv_attention_amd as tq
+    from tests import synth
+    from tests.gputil import gpu_store_all, to_dev
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config(args.workload)
+    N, B, Hq, Hk, S = cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"]
+    preset = cfg["preset"]
+    slot = tq.tqkv_slot_bytes(preset)
+    print("bench: workload %s, generating inputs" % args.workload, file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg)
+
+    # ---- device-resident inputs
+    base = gpu_store_all(cfg, inp, device=dev)
+    nbytes = base.nbytes
+    R = max(1, int(math.ceil(args.cold_mb * 2 ** 20 / nbytes)))
+    caches = [base]
+    for _ in range(R - 1):
+        caches.append(tq.Cache(preset, B, Hk, S, device=dev, buffer=base.buffer.clone()))
+    si, po = synth.token_lists(B, S, S - N, S)
+    Kn = to_dev(synth.rows(inp["K"], S - N, S), dev)
+    Vn = to_dev(synth.rows(inp["V"], S - N, S), dev)
+    si_d, po_d = to_dev(si, dev), to_dev(po, dev)
+    Q = to_dev(inp["Q"], dev)
+    sl = to_dev(inp["seq_lens"], dev)
+    out = torch.empty((N, B, Hq, 128), dtype=torch.float32, device=dev)
+    ws_bytes = tq.tqkv_verify_workspace_bytes(base, N, Hq, args.num_splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    splits = tq.tqkv_verify_num_splits(base, N, Hq, args.num_splits)
+    torch.cuda.synchronize()
+    del inp["K"], inp["V"]
+
+    def store(i):
+        tq.tqkv_store(caches[i % R], Kn, Vn, si_d, po_d)
+
+    def verify(i):
+        tq.tqkv_verify(caches[i % R], Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
+                       out=out, workspace=ws)
+
+    def step(i):
+        store(i)
+        verify(i)
+
+    def capture(fn, n, offset=0):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(offset + i)
+        return g
+
+    def time_graph(g):
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)  # ms
+
+    # ---- eager warmup (also loads the code objects), then graphs
+    for i in range(max(1, args.warmup)):
+        step(i)
+    torch.cuda.synchronize()
+    print("bench: capturing graphs (R=%d replicas of %.1f MB, splits=%d)" % (R, nbytes / 1e6, splits),
+          file=sys.stderr, flush=True)
+    g_warm = capture(step, max(1, args.warmup))
+    g_steps = capture(step, args.steps)
+    g_verify = capture(verify, args.kernel_calls)
+    g_store = capture(store, args.kernel_calls)
+    g_warm.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_steps.replay()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    print("bench: %d steps in %.3f ms" % (args.steps, wall_ms), file=sys.stderr, flush=True)
+
+    # per-launch durations with HIP events on the launch stream
+    verify_ms = min(time_graph(g_verify) for _ in range(3)) / args.kernel_calls
+    store_ms = min(time_graph(g_store) for _ in range(3)) / args.kernel_calls
+    # warm (MALL-resident) verify: one replica only
+    g_warmv = capture(lambda i: verify(0), args.kernel_calls)
+    verify_warm_ms = min(time_graph(g_warmv) for _ in range(3)) / args.kernel_calls
+    # eager steps, for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    kv_bytes = B * S * Hk * slot
+    qo_bytes = 2 * N * B * Hq * 128 * 4
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = (kv_bytes + qo_bytes) / (verify_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
+    pages_ms = PAGES_FUSED_TRITON_MS.get(args.workload)
+    rec = {
+        "metric": "verify-attention µs/call + effective KV GB/s (frac of HBM peak), PoC shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(pages_ms / verify_ms, 2) if pages_ms else None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: preset=%s N_spec=%d B=%d Hq=%d Hk=%d D=128 seqlen=%d causal=%s"
+                        % (args.workload, "k8v4" if preset == 1 else "k3v4_nc", N, B, Hq, Hk, S,
+                           cfg["causal"]),
+            "num_splits": splits,
+            "cold_replicas": R,
+            "step": "store(N_spec new tokens x B x Hk) + verify(all tokens)",
+            "timing": "HIP graph of K steps, one replay",
+        },
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_verify_call": round(verify_ms * 1e3, 3),
+        "us_per_store_call": round(store_ms * 1e3, 3),
+        "us_per_verify_call_mall_warm": round(verify_warm_ms * 1e3, 3),
+        "us_per_step_eager": round(eager_ms * 1e3, 3),
+        "kv_bytes_per_call": kv_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "tqkv_verify (verify_kernel + combine_kernel when splits > 1)",
+            "bytes_per_launch": kv_bytes + qo_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    if pages_ms:
+        rec["context_pages_b70_fused_triton_us"] = pages_ms * 1e3
+    print(json.dumps(rec))
+
+
+def cpu_baseline(cfg, seconds):
+    """The oracle (as it stands) timed on this host's cores on a sample of
+    the same workload: the full step for as many (b, hk) units as fit in
+    about `seconds` of CPU time."""
+    import oracle
+    from tests import synth
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    N, B, Hq, Hk, S = cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"]
+    preset = cfg["preset"]
+    inp = synth.make_inputs(cfg)
+    slot = oracle.slot_bytes(preset)
+    # sample: sequence 0 only (all of its KV heads), the whole sequence stored
+    # once outside the timing; the timed part is one step (store of the N new
+    # tokens + verify), repeated until `seconds` have passed
+    cache = np.zeros(oracle.cache_bytes(preset, 1, Hk, S), np.uint8)
+    si, po = synth.token_lists(1, S)
+    oracle.store(preset, cache, 1, Hk, S, synth.rows(inp["K"][:1]), synth.rows(inp["V"][:1]), si, po)
+    si_n, po_n = synth.token_lists(1, S, S - N, S)
+    Kn = synth.rows(inp["K"][:1], S - N, S)
+    Vn = synth.rows(inp["V"][:1], S - N, S)
+    Q = np.ascontiguousarray(inp["Q"][:, :1])
+    sl = inp["seq_lens"][:1]
+    reps, t_total = 0, 0.0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.store(preset, cache, 1, Hk, S, Kn, Vn, si_n, po_n)
+        oracle.verify(preset, cache, 1, Hk, S, Q, sl, Hq, cfg["causal"])
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 100:
+            break
+    per_step = t_total / reps
+    kv = 1 * S * Hk * slot
+    return {
+        "value": round(kv / per_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "one of %d sequences (all %d KV heads, %d tokens, %d queries each): store of the "
+                  "%d new tokens + binary64 verify, %d reps, %.3f s per step" % (
+                      B, Hk, S, N * Hq, N, reps, per_step),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * tqkv.h -- C ABI of libtqkv.so: TurboQuant KV-cache store and speculative
+ * verification attention for AMD Instinct MI355X (gfx950).
+ *
+ * The two calls follow the problem statement of "Speculative decoding on
+ * Intel Arc: TurboQuant KV + a fused N_spec kernel" (turboquant-xpu blog,
+ * 2026-04-14):
+ *   - tqkv_store  is the fused store (Context section: Walsh-Hadamard
+ *     rotation + Lloyd-Max codebook for keys, uniform scalar quantisation for
+ *     values; the k8v4 preset keeps FP8 keys, Part 6);
+ *   - tqkv_verify is the fused N_spec verification attention of Part 3
+ *     (query [N_spec, B, Hq, D] -> output of the same shape) with the causal
+ *     window of Part 4 (query n attends to cached_len + n + 1 tokens) and the
+ *     split-KV partition + log-sum-exp reduction of Part 2.
+ *
+ * Memory and streams.  Every pointer argument is device memory owned by the
+ * caller, except the tqkv_cache descriptor itself (host memory, read during
+ * the call only).  The library allocates nothing on the device, copies
+ * nothing between host and device, and never synchronises: each call
+ * enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns.  Calls are reentrant; the library keeps no state
+ * besides read-only constant tables.
+ *
+ * Errors.  Every entry point validates its host-side arguments first and
+ * returns a negative tqkv_status without launching anything when they are
+ * invalid.  TQKV_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ * Device-side values (seq_idx, pos, seq_lens) cannot be checked on the host
+ * without a synchronisation; the kernels clamp or skip out-of-range values so
+ * that no access leaves the caller's buffers, and the documented
+ * preconditions say what the result then is.
+ *
+ * Cache layout (all sizes for D = 128).  Per (sequence b, KV head hk) the
+ * tokens are cut into blocks of 16; block blk of (b, hk) starts at
+ *   base + ((b * Hk + hk) * nblk + blk) * tqkv_block_bytes(preset),
+ * nblk = ceil(max_seq / 16).  A k3v4_nc block is 1920 B (120 B per token:
+ * 48 B of 3-bit key codes, 64 B of 4-bit value codes, fp16 norm, fp16 norm
+ * correction, fp16 value scale, fp16 value zero); a k8v4 block is 3168 B
+ * (198 B per token: 128 B of FP8 E4M3 key codes, 64 B of value codes, fp16
+ * key scale, value scale, value zero).  The exact byte and bit placement is
+ * specified in the design notes of this repository; the stored bytes of a
+ * token depend only on that token's K and V.
+ */
+#ifndef TQKV_H
+#define TQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQKV_HEAD_DIM 128    /* the only supported head size */
+#define TQKV_BLOCK_TOKENS 16 /* tokens per cache block */
+#define TQKV_MAX_ROWS 64     /* (Hq / Hk) * n_spec must not exceed this */
+
+typedef enum {
+    TQKV_K8V4 = 1,    /* FP8 E4M3 keys with a per-token fp16 scale, 4-bit values */
+    TQKV_K3V4_NC = 2  /* WHT-rotated 3-bit Lloyd-Max keys + norm correction, 4-bit values */
+} tqkv_preset;
+
+typedef enum {
+    TQKV_Q_F32 = 0,
+    TQKV_Q_F16 = 1
+} tqkv_qtype;
+
+typedef enum {
+    TQKV_OK = 0,
+    TQKV_ERR_ARG = -1,         /* a null pointer, a negative size, a bad enum */
+    TQKV_ERR_UNSUPPORTED = -2, /* D != 128, too many rows per KV head, Hq % Hk != 0 */
+    TQKV_ERR_ALIGN = -3,       /* a device pointer is not aligned as documented */
+    TQKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+    TQKV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
+    TQKV_ERR_DEVICE = -6       /* no usable gfx950 device is current */
+} tqkv_status;
+
+/* A quantised KV cache in caller-owned device memory of
+ * tqkv_cache_bytes(preset, B, Hk, D, max_seq) bytes, 16-byte aligned. */
+typedef struct tqkv_cache {
+    int32_t preset;  /* tqkv_preset */
+    int32_t B;       /* sequences */
+    int32_t Hk;      /* KV heads */
+    int32_t D;       /* head size, must be 128 */
+    int32_t max_seq; /* token capacity per sequence */
+    void *base;      /* device pointer */
+} tqkv_cache;
+
+/* Bytes per token and KV head: 120 (k3v4_nc) or 198 (k8v4); 0 for a bad preset. */
+size_t tqkv_slot_bytes(int preset);
+
+/* Bytes per 16-token block: 16 * tqkv_slot_bytes(preset). */
+size_t tqkv_block_bytes(int preset);
+
+/* Bytes of a whole cache; 0 for invalid arguments. */
+size_t tqkv_cache_bytes(int preset, int B, int Hk, int D, int max_seq);
+
+/* store(K, V, codes): quantise T new tokens for all Hk heads into the cache.
+ *   K, V     device, fp16 [T, Hk, 128] (row-major), 2-byte aligned
+ *   seq_idx  device, int32 [T]: sequence of token t, in [0, B)
+ *   pos      device, int32 [T]: position of token t, in [0, max_seq)
+ * Keys (k3v4_nc): fp32 norm n, normalised Sylvester WHT of k/n, 3-bit code
+ * per coordinate against the N(0, 1/128) Lloyd-Max thresholds, norm
+ * correction gamma = 1/||c[codes]||, fp16 n and gamma.  Keys (k8v4): scale
+ * s = fp16(max|k| / 448), codes = e4m3(k / s) rounded to nearest even and
+ * saturated.  Values: zero = min v, scale = fp16((max v - min v) / 15),
+ * code = clamp(rint((v - zero) / scale), 0, 15).  The bytes written are
+ * bit-identical to the specification (all arithmetic IEEE binary32, RNE).
+ * (seq_idx, pos) pairs must be distinct within one call; an entry out of
+ * range is skipped (nothing written).  T == 0 is a no-op.
+ * Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_store(const tqkv_cache *cache, const void *K, const void *V, const int32_t *seq_idx,
+               const int32_t *pos, int T, void *stream);
+
+/* Number of key-range partitions tqkv_verify uses for num_splits (0 = auto)
+ * on this cache and shape; 0 for invalid arguments. */
+int tqkv_verify_num_splits(const tqkv_cache *cache, int n_spec, int Hq, int num_splits);
+
+/* Device workspace tqkv_verify needs (0 when it needs none); bytes are
+ * returned through *bytes.  Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int num_splits,
+                                size_t *bytes);
+
+/* verify(Q, cache, lens): attention of n_spec speculative queries per
+ * sequence over the quantised cache.
+ *   Q         device, [n_spec, B, Hq, 128] of q_dtype, 16-byte aligned
+ *   seq_lens  device, int32 [B]: tokens in the cache for sequence b, the
+ *             n_spec speculative ones included (cached_len = seq_lens[b] - n_spec)
+ *   causal    1: query n attends to tokens [0, cached_len + n + 1);
+ *             0: every query attends to tokens [0, seq_lens[b])
+ *   num_splits  key-range partitions per (b, hk), 0 = auto (at most 256 are used)
+ *   sm_scale  softmax scale, 0 = 1/sqrt(128)
+ *   out       device, fp32 [n_spec, B, Hq, 128], 16-byte aligned
+ *   workspace device, 16-byte aligned, >= tqkv_verify_workspace_bytes(...)
+ * Query head hq reads KV head hq / (Hq / Hk).  k3v4_nc queries are rotated by
+ * the same normalised WHT as the keys.  Preconditions (device values):
+ * n_spec <= seq_lens[b] <= max_seq and every token below seq_lens[b] was
+ * stored; a larger seq_lens[b] is clamped to max_seq, and a row that sees no
+ * token is NaN.  The result matches plain softmax attention over the
+ * dequantised cache up to fp16 rounding of the MFMA operands.
+ * Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens,
+                int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *tqkv_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int tqkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQKV_H */

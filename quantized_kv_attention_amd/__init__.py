@@ -1,0 +1,220 @@
+"""TurboQuant KV-cache store and speculative verification attention on
+AMD Instinct MI355X (gfx950).
+
+This module is a thin ctypes binding of ``libtqkv.so`` (C ABI in
+``include/tqkv.h``).  Every step of the computation runs in the library's HIP
+kernels; Python only marshals arguments.  PyTorch provides device memory and
+the current stream.  There is no fallback: if the library is missing or no
+gfx950 device is current, calls raise.
+
+Names mirror the C entry points::
+
+    tqkv_slot_bytes(preset)                 tqkv_block_bytes(preset)
+    tqkv_cache_bytes(preset, B, Hk, D, max_seq)
+    tqkv_store(cache, K, V, seq_idx, pos)
+    tqkv_verify_num_splits(cache, n_spec, Hq, num_splits)
+    tqkv_verify_workspace_bytes(cache, n_spec, Hq, num_splits)
+    tqkv_verify(cache, Q, seq_lens, n_spec, Hq, causal, ...)
+    tqkv_status_string(status)              tqkv_version()
+
+``Cache`` owns a device buffer and the descriptor the C calls take.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "K8V4", "K3V4_NC", "HEAD_DIM", "BLOCK_TOKENS", "TqkvError", "Cache", "library_path",
+    "tqkv_slot_bytes", "tqkv_block_bytes", "tqkv_cache_bytes", "tqkv_store",
+    "tqkv_verify_num_splits", "tqkv_verify_workspace_bytes", "tqkv_verify",
+    "tqkv_status_string", "tqkv_version",
+]
+
+K8V4 = 1
+K3V4_NC = 2
+HEAD_DIM = 128
+BLOCK_TOKENS = 16
+Q_F32 = 0
+Q_F16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libtqkv.so")
+
+
+class TqkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s failed: %s (status %d)" % (where, tqkv_status_string(status), status))
+        self.status = status
+
+
+class _CacheDesc(ctypes.Structure):
+    _fields_ = [("preset", ctypes.c_int32), ("B", ctypes.c_int32), ("Hk", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("base", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError("libtqkv.so not found at %s; build it with __graft_entry__.build()"
+                          % library_path)
+    L = ctypes.CDLL(library_path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    S = ctypes.c_size_t
+    D = ctypes.POINTER(_CacheDesc)
+    L.tqkv_slot_bytes.argtypes = [I]
+    L.tqkv_slot_bytes.restype = S
+    L.tqkv_block_bytes.argtypes = [I]
+    L.tqkv_block_bytes.restype = S
+    L.tqkv_cache_bytes.argtypes = [I, I, I, I, I]
+    L.tqkv_cache_bytes.restype = S
+    L.tqkv_store.argtypes = [D, P, P, P, P, I, P]
+    L.tqkv_store.restype = I
+    L.tqkv_verify_num_splits.argtypes = [D, I, I, I]
+    L.tqkv_verify_num_splits.restype = I
+    L.tqkv_verify_workspace_bytes.argtypes = [D, I, I, I, ctypes.POINTER(S)]
+    L.tqkv_verify_workspace_bytes.restype = I
+    L.tqkv_verify.argtypes = [D, P, I, P, I, I, I, I, ctypes.c_float, P, P, S, P]
+    L.tqkv_verify.restype = I
+    L.tqkv_status_string.argtypes = [I]
+    L.tqkv_status_string.restype = ctypes.c_char_p
+    L.tqkv_version.argtypes = []
+    L.tqkv_version.restype = I
+    _lib = L
+    return L
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtqkv.so (raises ImportError when it is not built)."""
+    return _load()
+
+
+# ---------------------------------------------------------------- sizes ---
+
+def tqkv_slot_bytes(preset: int) -> int:
+    return int(_load().tqkv_slot_bytes(preset))
+
+
+def tqkv_block_bytes(preset: int) -> int:
+    return int(_load().tqkv_block_bytes(preset))
+
+
+def tqkv_cache_bytes(preset: int, B: int, Hk: int, D: int, max_seq: int) -> int:
+    return int(_load().tqkv_cache_bytes(preset, B, Hk, D, max_seq))
+
+
+def tqkv_status_string(status: int) -> str:
+    return _load().tqkv_status_string(status).decode()
+
+
+def tqkv_version() -> int:
+    return int(_load().tqkv_version())
+
+
+# ---------------------------------------------------------------- cache ---
+
+class Cache:
+    """A quantised KV cache in device memory (uint8 tensor) + its descriptor."""
+
+    def __init__(self, preset: int, B: int, Hk: int, max_seq: int, device="cuda", buffer=None):
+        nbytes = tqkv_cache_bytes(preset, B, Hk, HEAD_DIM, max_seq)
+        if nbytes == 0:
+            raise ValueError("invalid cache shape")
+        if buffer is None:
+            buffer = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        if buffer.dtype != torch.uint8 or buffer.numel() != nbytes or not buffer.is_contiguous():
+            raise ValueError("cache buffer must be a contiguous uint8 tensor of %d bytes" % nbytes)
+        self.preset, self.B, self.Hk, self.max_seq = preset, B, Hk, max_seq
+        self.buffer = buffer
+        self.desc = _CacheDesc(preset, B, Hk, HEAD_DIM, max_seq, buffer.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        return self.buffer.numel()
+
+
+def _stream_ptr(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TqkvError(status, where)
+
+
+# ---------------------------------------------------------------- store ---
+
+def tqkv_store(cache: Cache, K: torch.Tensor, V: torch.Tensor, seq_idx: torch.Tensor,
+               pos: torch.Tensor, stream=None) -> None:
+    """Quantise K, V (fp16 [T, Hk, 128], device) into ``cache`` at
+    (seq_idx[t], pos[t]) (int32 [T], device); enqueued on ``stream``."""
+    T = K.shape[0]
+    if K.dtype != torch.float16 or V.dtype != torch.float16:
+        raise TypeError("K and V must be float16")
+    if K.shape != (T, cache.Hk, HEAD_DIM) or V.shape != K.shape:
+        raise ValueError("K and V must have shape [T, Hk, 128]")
+    if seq_idx.dtype != torch.int32 or pos.dtype != torch.int32:
+        raise TypeError("seq_idx and pos must be int32")
+    if seq_idx.shape != (T,) or pos.shape != (T,):
+        raise ValueError("seq_idx and pos must have shape [T]")
+    for x in (K, V, seq_idx, pos):
+        if not x.is_contiguous() or x.device != cache.buffer.device:
+            raise ValueError("tensors must be contiguous and on the cache's device")
+    st = _load().tqkv_store(ctypes.byref(cache.desc), K.data_ptr(), V.data_ptr(), seq_idx.data_ptr(),
+                            pos.data_ptr(), T, _stream_ptr(K, stream))
+    _check(st, "tqkv_store")
+
+
+# --------------------------------------------------------------- verify ---
+
+def tqkv_verify_num_splits(cache: Cache, n_spec: int, Hq: int, num_splits: int = 0) -> int:
+    return int(_load().tqkv_verify_num_splits(ctypes.byref(cache.desc), n_spec, Hq, num_splits))
+
+
+def tqkv_verify_workspace_bytes(cache: Cache, n_spec: int, Hq: int, num_splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    st = _load().tqkv_verify_workspace_bytes(ctypes.byref(cache.desc), n_spec, Hq, num_splits,
+                                             ctypes.byref(n))
+    _check(st, "tqkv_verify_workspace_bytes")
+    return int(n.value)
+
+
+def tqkv_verify(cache: Cache, Q: torch.Tensor, seq_lens: torch.Tensor, n_spec: int, Hq: int,
+                causal: bool, num_splits: int = 0, sm_scale: float = 0.0,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """Verification attention; returns ``out`` (fp32 [n_spec, B, Hq, 128])."""
+    if Q.dtype == torch.float32:
+        qd = Q_F32
+    elif Q.dtype == torch.float16:
+        qd = Q_F16
+    else:
+        raise TypeError("Q must be float32 or float16")
+    if Q.shape != (n_spec, cache.B, Hq, HEAD_DIM) or not Q.is_contiguous():
+        raise ValueError("Q must be a contiguous [n_spec, B, Hq, 128] tensor")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (cache.B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if out is None:
+        out = torch.empty((n_spec, cache.B, Hq, HEAD_DIM), dtype=torch.float32, device=Q.device)
+    if out.dtype != torch.float32 or out.shape != Q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like Q")
+    need = tqkv_verify_workspace_bytes(cache, n_spec, Hq, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _load().tqkv_verify(ctypes.byref(cache.desc), Q.data_ptr(), qd, seq_lens.data_ptr(), n_spec,
+                             Hq, int(bool(causal)), num_splits, float(sm_scale), out.data_ptr(),
+                             ws_ptr, ws_len, _stream_ptr(Q, stream))
+    _check(st, "tqkv_verify")
+    return out

@@ -1,0 +1,87 @@
+// Shared definitions of the HIP library: cache layout constants, launch
+// descriptors and small device helpers.  Host and device code include it.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace tqkv {
+
+constexpr int kD = 128;
+constexpr int kBlockTokens = 16;
+constexpr int kPresetK8V4 = 1;
+constexpr int kPresetK3V4 = 2;
+constexpr int kMaxRows = 64;
+
+// Byte layout of one 16-token block (see include/tqkv.h for the overview).
+//   k3v4_nc: key codes [0,768) 48 B/token | value nibbles [768,1792) |
+//            n_h[16] @1792 | gamma_h[16] @1824 | vscale[16] @1856 | vzero[16] @1888
+//   k8v4:    e4m3 keys [0,2048) 128 B/token | value nibbles [2048,3072) |
+//            kscale[16] @3072 | vscale[16] @3104 | vzero[16] @3136
+template <int P> struct Layout;
+template <> struct Layout<kPresetK3V4> {
+    static constexpr int kBlockBytes = 1920;
+    static constexpr int kKeyBytesPerToken = 48;
+    static constexpr int kValOff = 768;
+    static constexpr int kMeta0 = 1792; // n_h
+    static constexpr int kMeta1 = 1824; // gamma_h
+    static constexpr int kVScale = 1856;
+    static constexpr int kVZero = 1888;
+};
+template <> struct Layout<kPresetK8V4> {
+    static constexpr int kBlockBytes = 3168;
+    static constexpr int kKeyBytesPerToken = 128;
+    static constexpr int kValOff = 2048;
+    static constexpr int kMeta0 = 3072; // kscale_h
+    static constexpr int kMeta1 = -1;
+    static constexpr int kVScale = 3104;
+    static constexpr int kVZero = 3136;
+};
+
+// Value nibble byte p (coordinates 2p | 2p+1) of block token tb lives at this
+// offset inside the value region: dword ((i*2+h)*2+e)*2+q with i = p/2,
+// e = p%2, h = tb/8, q = (tb/4)%2, byte {0,2,1,3}[tb%4] of that dword.  The
+// order lets one 16-byte load per lane of a wavefront fetch, for 32 d-quads
+// x 2 token halves, exactly the 8-token runs an MFMA operand needs.
+__host__ __device__ inline int val_byte_offset(int tb, int p)
+{
+    int dw = (((p >> 1) * 2 + (tb >> 3)) * 2 + (p & 1)) * 2 + ((tb >> 2) & 1);
+    int pos = ((tb & 1) << 1) | ((tb >> 1) & 1);
+    return dw * 4 + pos;
+}
+
+struct StoreArgs {
+    uint8_t *base;
+    const uint16_t *K;
+    const uint16_t *V;
+    const int32_t *seq_idx;
+    const int32_t *pos;
+    int B, Hk, max_seq, nblk, T;
+};
+
+struct VerifyArgs {
+    const uint8_t *base;
+    const void *Q;
+    const int32_t *seq_lens;
+    float *out;      // final output (nsplit == 1)
+    float *part_o;   // [units * nsplit * R][128] normalised partial outputs
+    float2 *part_ml; // [units * nsplit * R] (running max in log2 units, softmax sum)
+    int Hk, max_seq, nblk;
+    int q_f16;
+    int B, N, Hq, G, R, causal, nsplit;
+    float qscale; // sm_scale * log2(e)
+};
+
+struct CombineArgs {
+    const float *part_o;
+    const float2 *part_ml;
+    float *out;
+    int B, Hk, N, Hq, G, R, nsplit;
+};
+
+// Launchers (defined next to their kernels).
+hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
+hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+} // namespace tqkv

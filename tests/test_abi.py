@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/tqkv.h declares, sizes follow the documented
+layout, and invalid arguments are rejected before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_kv_attention_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tqkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tqkv_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 8
+    L = ctypes.CDLL(tq.library_path)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_names_match_header():
+    for n in _declared():
+        assert hasattr(tq, n), n
+
+
+def test_sizes():
+    assert tq.tqkv_slot_bytes(tq.K3V4_NC) == 120
+    assert tq.tqkv_slot_bytes(tq.K8V4) == 198
+    assert tq.tqkv_slot_bytes(7) == 0
+    assert tq.tqkv_block_bytes(tq.K3V4_NC) == 1920
+    assert tq.tqkv_block_bytes(tq.K8V4) == 3168
+    # PoC shape: B=4, Hk=4, 8192 tokens
+    assert tq.tqkv_cache_bytes(tq.K3V4_NC, 4, 4, 128, 8192) == 4 * 4 * 8192 * 120
+    assert tq.tqkv_cache_bytes(tq.K8V4, 4, 4, 128, 8192) == 4 * 4 * 8192 * 198
+    assert tq.tqkv_cache_bytes(tq.K8V4, 1, 1, 128, 17) == 2 * 3168  # partial block rounds up
+    assert tq.tqkv_cache_bytes(tq.K8V4, 1, 1, 64, 16) == 0
+    assert tq.tqkv_cache_bytes(tq.K8V4, 0, 1, 128, 16) == 0
+    assert tq.tqkv_version() >= 100
+
+
+def _desc(**kw):
+    d = dict(preset=tq.K8V4, B=1, Hk=1, D=128, max_seq=16, base=4096)
+    d.update(kw)
+    return tq._CacheDesc(d["preset"], d["B"], d["Hk"], d["D"], d["max_seq"], d["base"])
+
+
+def test_status_strings():
+    for s in range(-6, 1):
+        assert tq.tqkv_status_string(s) != "unknown status"
+    assert tq.tqkv_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(preset=3), -1), (dict(B=0), -1), (dict(base=0), -1), (dict(D=64), -2),
+    (dict(base=4100), -3),
+])
+def test_store_rejects_bad_cache(kw, status):
+    L = tq.lib()
+    d = _desc(**kw)
+    assert L.tqkv_store(ctypes.byref(d), 4096, 4096, 4096, 4096, 1, None) == status
+
+
+def test_store_rejects_bad_arguments():
+    L = tq.lib()
+    d = _desc()
+    assert L.tqkv_store(None, 4096, 4096, 4096, 4096, 1, None) == -1
+    assert L.tqkv_store(ctypes.byref(d), 4096, 4096, 4096, 4096, -1, None) == -1
+    assert L.tqkv_store(ctypes.byref(d), None, 4096, 4096, 4096, 1, None) == -1
+    assert L.tqkv_store(ctypes.byref(d), 4097, 4096, 4096, 4096, 1, None) == -3
+    assert L.tqkv_store(ctypes.byref(d), 4096, 4096, 4098, 4096, 1, None) == -3
+    assert L.tqkv_store(ctypes.byref(d), None, None, None, None, 0, None) == 0  # T == 0: no-op
+
+
+def test_verify_rejects_bad_arguments():
+    L = tq.lib()
+    d = _desc(Hk=2)
+    ok = dict(Q=4096, qd=0, sl=4096, n=8, Hq=16, causal=1, ns=0, sc=0.0, out=4096)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.tqkv_verify(ctypes.byref(d), a["Q"], a["qd"], a["sl"], a["n"], a["Hq"], a["causal"],
+                             a["ns"], a["sc"], a["out"], None, 0, None)
+
+    assert call(Q=None) == -1
+    assert call(sl=None) == -1
+    assert call(out=None) == -1
+    assert call(qd=2) == -1
+    assert call(causal=2) == -1
+    assert call(n=0) == -1
+    assert call(ns=-1) == -1
+    assert call(sc=-1.0) == -1
+    assert call(sc=float("inf")) == -1
+    assert call(sc=float("nan")) == -1
+    assert call(Hq=15) == -2            # Hq % Hk != 0
+    assert call(n=9) == -2              # (16/2) * 9 = 72 rows > 64
+    assert call(Q=4104) == -3           # Q must be 16-byte aligned
+    assert call(out=4100) == -3
+    n = ctypes.c_size_t(7)
+    assert L.tqkv_verify_workspace_bytes(ctypes.byref(d), 8, 15, 0, ctypes.byref(n)) == -2
+    assert n.value == 0
+    assert L.tqkv_verify_workspace_bytes(ctypes.byref(d), 8, 16, 0, None) == -1
+    assert L.tqkv_verify_num_splits(ctypes.byref(d), 0, 16, 0) == 0

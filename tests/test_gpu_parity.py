@@ -1,0 +1,231 @@
+"""GPU parity of the HIP library against the CPU oracle (run with -m gpu).
+
+Codes: the whole physical cache written by tqkv_store must equal, byte for
+byte, the cache the oracle writes from the same fp16 inputs.  Outputs:
+tqkv_verify must match the oracle's binary64 attention within atol 5e-3,
+rtol 1e-2 (the tolerance of the pages' integration test, Part 6 of
+"Speculative decoding on Intel Arc: TurboQuant KV + a fused N_spec kernel"),
+with NaN exactly where the oracle has NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import synth
+from tests.gputil import assert_close, gpu_store_all, oracle_unit, to_dev
+
+pytestmark = pytest.mark.gpu
+
+tq = pytest.importorskip("quantized_kv_attention_amd")
+
+PRESETS = [synth.K8V4, synth.K3V4_NC]
+PNAME = {synth.K8V4: "k8v4", synth.K3V4_NC: "k3v4_nc"}
+
+
+def _small(preset, **kw):
+    cfg = dict(preset=preset, N=8, B=2, Hq=16, Hk=2, S=203, causal=True, q_dtype=np.float32, seed=7)
+    cfg.update(kw)
+    return cfg
+
+
+def _oracle_cache(cfg, inp, max_seq=None):
+    B, S, Hk = cfg["B"], cfg["S"], cfg["Hk"]
+    max_seq = max_seq or S
+    cache = np.zeros(oracle.cache_bytes(cfg["preset"], B, Hk, max_seq), np.uint8)
+    si, po = synth.token_lists(B, S)
+    oracle.store(cfg["preset"], cache, B, Hk, max_seq, synth.rows(inp["K"]), synth.rows(inp["V"]), si, po)
+    return cache
+
+
+def _gpu_verify(cache, cfg, inp, **kw):
+    Q = to_dev(inp["Q"])
+    sl = to_dev(inp["seq_lens"])
+    out = tq.tqkv_verify(cache, Q, sl, cfg["N"], cfg["Hq"], cfg["causal"], **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# ------------------------------------------------------------------ store ---
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("seed", [0] + list(synth.HELD_OUT_SEEDS))
+def test_store_bit_exact_small(preset, seed):
+    cfg = _small(preset, seed=seed)
+    inp = synth.make_inputs(cfg)
+    print("store small", PNAME[preset], "seed", seed, flush=True)
+    ref = _oracle_cache(cfg, inp)
+    got = gpu_store_all(cfg, inp).buffer.cpu().numpy()
+    assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
+
+
+@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc"])
+def test_store_bit_exact_config(name):
+    cfg = synth.config(name)
+    inp = synth.make_inputs(cfg)
+    print("store", name, flush=True)
+    ref = _oracle_cache(cfg, inp)
+    got = gpu_store_all(cfg, inp).buffer.cpu().numpy()
+    assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_store_edge_vectors(preset):
+    """Zero, constant, tiny, huge, mixed-sign-zero and tie-prone vectors."""
+    rng = np.random.default_rng(99)
+    vecs = [
+        np.zeros(128), np.full(128, 1.5), np.full(128, -3.0), rng.standard_normal(128) * 1e-4,
+        rng.standard_normal(128) * 3e4, np.where(rng.random(128) < 0.5, 0.0, -0.0),
+        np.round(rng.standard_normal(128) * 4) / 4, np.arange(128) - 64.0, (np.arange(128) % 16) * 0.5,
+        rng.standard_normal(128) * 1e-6,
+    ]
+    T = len(vecs)
+    K = np.stack(vecs).astype(np.float16)[:, None, :]
+    V = np.stack(vecs[::-1]).astype(np.float16)[:, None, :]
+    si = np.zeros(T, np.int32)
+    po = (np.arange(T, dtype=np.int32) * 5) % 37  # scattered, distinct positions
+    ref = np.zeros(oracle.cache_bytes(preset, 1, 1, 40), np.uint8)
+    oracle.store(preset, ref, 1, 1, 40, K, V, si, po)
+    cache = tq.Cache(preset, 1, 1, 40)
+    tq.tqkv_store(cache, to_dev(K), to_dev(V), to_dev(si), to_dev(po))
+    got = cache.buffer.cpu().numpy()
+    assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
+
+
+def test_store_skips_out_of_range_and_empty():
+    cache = tq.Cache(synth.K8V4, 2, 1, 20)
+    K = torch.ones((3, 1, 128), dtype=torch.float16, device="cuda")
+    si = torch.tensor([0, 2, -1], dtype=torch.int32, device="cuda")
+    po = torch.tensor([20, 0, 3], dtype=torch.int32, device="cuda")
+    tq.tqkv_store(cache, K, K, si, po)
+    tq.tqkv_store(cache, K[:0], K[:0], si[:0], po[:0])
+    torch.cuda.synchronize()
+    assert int(cache.buffer.count_nonzero()) == 0
+
+
+# ----------------------------------------------------------------- verify ---
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("q_dtype", [np.float32, np.float16])
+def test_verify_small(preset, causal, q_dtype):
+    cfg = _small(preset, causal=causal, q_dtype=q_dtype)
+    inp = synth.make_inputs(cfg)
+    inp["seq_lens"] = np.array([203, 150], np.int32)  # ragged: a tail tile, two lengths
+    print("verify small", PNAME[preset], causal, q_dtype.__name__, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"], inp["seq_lens"],
+                        cfg["Hq"], causal)
+    cache = gpu_store_all(cfg, inp)
+    for ns in (0, 1, 2, 3):
+        got = _gpu_verify(cache, cfg, inp, num_splits=ns)
+        assert_close(got, ref, what="num_splits=%d" % ns)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("shape", [
+    dict(N=1, Hq=1, Hk=1, B=1, S=17),          # one row, partial block
+    dict(N=1, Hq=32, Hk=8, B=3, S=100),        # plain decode, 4 rows per KV head
+    dict(N=3, Hq=11, Hk=1, B=1, S=64),         # 33 rows: two row tiles, padding
+    dict(N=16, Hq=4, Hk=1, B=1, S=300),        # 64 rows from a long window
+    dict(N=2, Hq=6, Hk=6, B=2, S=48),          # MHA
+    dict(N=8, Hq=8, Hk=1, B=1, S=8),           # the whole sequence is speculative
+], ids=lambda s: "N%d_Hq%d_Hk%d_B%d_S%d" % (s["N"], s["Hq"], s["Hk"], s["B"], s["S"]))
+def test_verify_shapes(preset, shape):
+    cfg = _small(preset, **shape)
+    inp = synth.make_inputs(cfg)
+    print("verify shape", PNAME[preset], shape, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"], inp["seq_lens"],
+                        cfg["Hq"], True)
+    cache = gpu_store_all(cfg, inp)
+    assert_close(_gpu_verify(cache, cfg, inp), ref, what=str(shape))
+
+
+@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc"])
+def test_verify_config_full(name):
+    """Every output of the small configurations against the oracle, in the
+    launch configuration the benchmark times (auto splits)."""
+    cfg = synth.config(name)
+    inp = synth.make_inputs(cfg)
+    print("verify", name, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(cfg["preset"], ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"],
+                        inp["seq_lens"], cfg["Hq"], cfg["causal"])
+    cache = gpu_store_all(cfg, inp)
+    got = _gpu_verify(cache, cfg, inp)
+    assert_close(got, ref, what=name)
+    # the pages' configured split count (8) gives the same answer
+    assert_close(_gpu_verify(cache, cfg, inp, num_splits=8), ref, what=name + " splits=8")
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["decode_k3v4_nc", "long_k3v4_nc"])
+def test_verify_config_sampled(name):
+    """Large configurations: full GPU run, oracle on sampled (b, hk) units."""
+    cfg = synth.config(name)
+    print("verify sampled", name, "generating inputs", flush=True)
+    inp = synth.make_inputs(cfg)
+    cache = gpu_store_all(cfg, inp)
+    got = _gpu_verify(cache, cfg, inp)
+    del cache
+    torch.cuda.empty_cache()
+    G = cfg["Hq"] // cfg["Hk"]
+    rng = np.random.default_rng(5)
+    units = [(0, 0), (cfg["B"] - 1, cfg["Hk"] - 1)] + [
+        (int(rng.integers(cfg["B"])), int(rng.integers(cfg["Hk"]))) for _ in range(2)]
+    for b, hk in units:
+        heads = [hk * G, hk * G + G - 1]
+        print("  oracle unit", b, hk, heads, flush=True)
+        ref = oracle_unit(oracle, cfg, inp, b, hk, heads=heads)
+        assert_close(got[:, b, heads], ref, what="%s b=%d hk=%d" % (name, b, hk))
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_verify_nan_parity(preset):
+    """A NaN key element poisons exactly the rows that can see its token."""
+    cfg = _small(preset, B=1, Hk=1, Hq=2, N=8, S=64)
+    inp = synth.make_inputs(cfg)
+    inp["K"][0, 60, 0, 5] = np.float16(np.nan)  # position 60: row n sees 57 + n tokens
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, 1, 1, 64, inp["Q"], inp["seq_lens"], 2, True)
+    assert np.isnan(ref[4:]).all() and not np.isnan(ref[:4]).any()
+    cache = gpu_store_all(cfg, inp)
+    for ns in (1, 3):
+        assert_close(_gpu_verify(cache, cfg, inp, num_splits=ns), ref, what="nan splits=%d" % ns)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_verify_causality_and_determinism(preset):
+    cfg = _small(preset)
+    inp = synth.make_inputs(cfg)
+    cache = gpu_store_all(cfg, inp)
+    a = _gpu_verify(cache, cfg, inp)
+    b = _gpu_verify(cache, cfg, inp)
+    assert np.array_equal(a, b)  # bitwise reproducible for a fixed launch
+    # rewrite the last two tokens: rows n < N-2 must not change
+    S, N = cfg["S"], cfg["N"]
+    inp2 = dict(inp)
+    inp2["K"] = inp["K"].copy()
+    inp2["V"] = inp["V"].copy()
+    inp2["K"][:, S - 2:] *= -3
+    inp2["V"][:, S - 2:] += 5
+    si, po = synth.token_lists(cfg["B"], S, S - 2, S)
+    tq.tqkv_store(cache, to_dev(synth.rows(inp2["K"], S - 2, S)), to_dev(synth.rows(inp2["V"], S - 2, S)),
+                  to_dev(si), to_dev(po))
+    c = _gpu_verify(cache, cfg, inp)
+    assert np.array_equal(a[:N - 2], c[:N - 2])
+    assert not np.allclose(a[N - 2:], c[N - 2:])
+
+
+def test_verify_rejects_bad_workspace():
+    cfg = _small(synth.K8V4)
+    inp = synth.make_inputs(cfg)
+    cache = gpu_store_all(cfg, inp)
+    need = tq.tqkv_verify_workspace_bytes(cache, cfg["N"], cfg["Hq"], 3)
+    assert need > 0
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tq.TqkvError) as e:
+        tq.tqkv_verify(cache, to_dev(inp["Q"]), to_dev(inp["seq_lens"]), cfg["N"], cfg["Hq"], True,
+                       num_splits=3, workspace=small)
+    assert e.value.status == -4
