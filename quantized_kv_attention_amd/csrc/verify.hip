@@ -31,6 +31,8 @@
 #include "codebook.h"
 #include "common.h"
 
+#include <type_traits>
+
 namespace tqkv {
 namespace {
 
@@ -41,7 +43,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;        // tokens per inner-loop step
 constexpr int kWaves = 4;        // wavefronts per work-group
-constexpr int kQStride = 136;    // halfs per query row in LDS (128 + pad)
+constexpr int kQStride = kQPadHalfs; // halfs per query row in LDS (128 + pad)
 constexpr int kAccStride = 132;  // floats per row of the LDS merge buffer
 
 union H8 {
@@ -138,30 +140,29 @@ template <int PRESET>
 __device__ inline void issue_tile(const uint8_t *ubase, int kt, int nblk, uint8_t *slot, int lane)
 {
     using L = Layout<PRESET>;
-    const int nb = min(2, nblk - 2 * kt);
-    const int valid = nb * L::kBlockBytes;
+    // the tile's bytes [0, valid); loads past the end re-read the final 16 B
+    const int valid = min(2, nblk - 2 * kt) * L::kBlockBytes;
     const uint8_t *src = ubase + (size_t)(2 * kt) * L::kBlockBytes;
     const uint32_t lds = (uint32_t)(size_t)(lds_void_t *)slot;
 #pragma unroll
     for (int j = 0; j < Ring<PRESET>::kLoads; ++j) {
-        int off = 1024 * j + 16 * lane;
-        off = off + 16 > valid ? valid - 16 : off;
-        dma16(src + off, lds + 1024 * j);
+        dma16(src + min(1024 * j + 16 * lane, valid - 16), lds + 1024 * j);
     }
 }
 
-// Registers of one tile, read back from its ring slot.
-template <int PRESET> struct Tile;
-template <> struct Tile<kPresetK3V4> {
-    uint2 k[3];        // 24 B: this lane's 64 key codes (two 32-code dword triples)
-    u32x4 v[2];        // value nibbles of blocks 0/1 (8-token runs at 4 d's)
-    u32x4 m0[2], m1[2]; // n_h, gamma_h of tokens 8h..8h+7, blocks 0/1
-    u32x4 vs[2], vz[2];
+// Registers of one tile, read back from its ring slot: the key half (the A
+// operands of S^T = K Q^T) and the value half (value nibbles and per-token
+// fields), read at different times by the software pipeline below.
+template <int PRESET> struct KeyRegs;
+template <> struct KeyRegs<kPresetK3V4> {
+    uint2 k[3]; // 24 B: this lane's 64 key codes (two 32-code dword triples)
 };
-template <> struct Tile<kPresetK8V4> {
-    u32x4 k[4];        // 64 B: this lane's 64 e4m3 key codes
-    u32x4 v[2];
-    u32x4 m0[2];       // kscale_h
+template <> struct KeyRegs<kPresetK8V4> {
+    u32x4 k[4]; // 64 B: this lane's 64 e4m3 key codes
+};
+struct ValRegs {
+    u32x4 v[2];  // value nibbles of blocks 0/1 (8-token runs at 4 d's)
+    u32x4 kf[2]; // per-token key factor (fp16): n*gamma (k3v4_nc) or kscale (k8v4), tokens 8h..8h+7
     u32x4 vs[2], vz[2];
 };
 
@@ -175,7 +176,7 @@ __device__ inline int tile_token_of_row(int m)
 }
 
 template <int PRESET>
-__device__ inline void read_tile(Tile<PRESET> &t, const uint8_t *slot, int lane)
+__device__ inline void read_keys(KeyRegs<PRESET> &t, const uint8_t *slot, int lane)
 {
     using L = Layout<PRESET>;
     const int h = lane >> 5, m = lane & 31;
@@ -190,13 +191,38 @@ __device__ inline void read_tile(Tile<PRESET> &t, const uint8_t *slot, int lane)
         for (int j = 0; j < 4; ++j)
             t.k[j] = *reinterpret_cast<const u32x4 *>(kb + 64 * h + 16 * j);
     }
+}
+
+__device__ inline uint32_t hmul2(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
+}
+
+template <int PRESET>
+__device__ inline void read_values(ValRegs &t, const uint8_t *slot, int lane)
+{
+    using L = Layout<PRESET>;
+    const int h = lane >> 5, m = lane & 31;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const uint8_t *bs = slot + s * L::kBlockBytes;
         t.v[s] = *reinterpret_cast<const u32x4 *>(bs + L::kValOff + (2 * m + h) * 16);
-        t.m0[s] = *reinterpret_cast<const u32x4 *>(bs + L::kMeta0 + 16 * h);
-        if constexpr (PRESET == kPresetK3V4)
-            t.m1[s] = *reinterpret_cast<const u32x4 *>(bs + L::kMeta1 + 16 * h);
+        const u32x4 n = *reinterpret_cast<const u32x4 *>(bs + L::kMeta0 + 16 * h);
+        if constexpr (PRESET == kPresetK3V4) {
+            // n * gamma per token, as fp16 pairs (one v_pk_mul_f16 per pair).
+            // Written component by component: an in-place update of vector
+            // elements in a loop (kf[s][j] = f(kf[s][j], g[j])) was
+            // miscompiled by this toolchain (only g[0] was loaded).
+            const u32x4 g = *reinterpret_cast<const u32x4 *>(bs + L::kMeta1 + 16 * h);
+            u32x4 kf;
+            kf.x = hmul2(n.x, g.x);
+            kf.y = hmul2(n.y, g.y);
+            kf.z = hmul2(n.z, g.z);
+            kf.w = hmul2(n.w, g.w);
+            t.kf[s] = kf;
+        } else {
+            t.kf[s] = n;
+        }
         t.vs[s] = *reinterpret_cast<const u32x4 *>(bs + L::kVScale + 16 * h);
         t.vz[s] = *reinterpret_cast<const u32x4 *>(bs + L::kVZero + 16 * h);
     }
@@ -205,7 +231,7 @@ __device__ inline void read_tile(Tile<PRESET> &t, const uint8_t *slot, int lane)
 // A operand of k-step ks of S^T = K Q^T: coordinates 64h + 8ks + 0..7 of
 // this lane's token.
 template <int PRESET>
-__device__ inline half8_t key_operand(const Tile<PRESET> &t, int ks)
+__device__ inline half8_t key_operand(const KeyRegs<PRESET> &t, int ks)
 {
     H8 o;
     if constexpr (PRESET == kPresetK3V4) {
@@ -241,31 +267,47 @@ __device__ inline half8_t key_operand(const Tile<PRESET> &t, int ks)
     return o.h;
 }
 
+// S^T = K Q^T for one tile.  The query B operands are re-read from the LDS
+// query tile (qrow points at this lane's row and half) instead of being held
+// in 8*NQT*4 VGPRs across the whole loop.
+template <int PRESET, int NQT>
+__device__ inline void qk_tile(const KeyRegs<PRESET> &k, const _Float16 *qrow, floatx16 (&S)[NQT])
+{
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+        S[qt] = floatx16{0};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const half8_t A = key_operand<PRESET>(k, ks);
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            const half8_t Bq = *reinterpret_cast<const half8_t *>(qrow + 32 * qt * kQStride + 8 * ks);
+            S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bq, S[qt], 0, 0, 0);
+        }
+    }
+}
+
 // A operand of O^T += V^T P^T for d-tile dt (d = 4i + dt) and k-step s
-// (tokens 16s + 8h + 0..7): the value codes as binary16 integers, c for the
-// low nibbles (even dt) and 16c for the high nibbles (odd dt).  Each
-// half-pair is (1024 + x) built by OR-ing the nibble under 0x6400 and then
-// 1024 subtracted exactly.
-template <int PRESET>
-__device__ inline half8_t value_operand(const Tile<PRESET> &t, int dt, int s)
+// (tokens 16s + 8h + 0..7).  The nibbles are used as binary16 bit patterns:
+// a low nibble c is the subnormal c * 2^-24, a high nibble the subnormal
+// 16c * 2^-24 (gfx950's f16 MFMA multiplies subnormal inputs exactly), so
+// one mask per half-pair builds the operand; the epilogue rescales even d by
+// 2^24 and odd d by 2^20.
+__device__ inline half8_t value_operand(const ValRegs &t, int dt, int s)
 {
     const int e = dt >> 1;
     const uint32_t mask = (dt & 1) ? 0x00F000F0u : 0x000F000Fu;
     const uint32_t wa = t.v[s][2 * e], wb = t.v[s][2 * e + 1];
     H8 o;
-    o.u[0] = (wa & mask) | 0x64006400u;
-    o.u[1] = ((wa >> 8) & mask) | 0x64006400u;
-    o.u[2] = (wb & mask) | 0x64006400u;
-    o.u[3] = ((wb >> 8) & mask) | 0x64006400u;
-    const half8_t bias = {(_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f,
-                          (_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f, (_Float16)1024.0f};
-    return o.h - bias;
+    o.u[0] = wa & mask;
+    o.u[1] = (wa >> 8) & mask;
+    o.u[2] = wb & mask;
+    o.u[3] = (wb >> 8) & mask;
+    return o.h;
 }
 
-__device__ inline uint16_t half_of(const u32x4 &v, int u)
-{
-    return (uint16_t)(v[u >> 1] >> (16 * (u & 1)));
-}
+__device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
+__device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
 
 // Lazy rescaling: the running row maximum m only moves when a tile's maximum
 // exceeds it by more than kRescaleSlack (log2 units), so probabilities are
@@ -273,19 +315,164 @@ __device__ inline uint16_t half_of(const u32x4 &v, int u)
 // min-max scale is), P * vscale <= 4 * 8736 stays inside binary16 range.
 constexpr float kRescaleSlack = 2.0f;
 
+// Online-softmax state of the lane's query rows (one per 32-row tile).
+template <int NQT> struct SoftState {
+    float m[NQT], l[NQT], z[NQT];
+};
+
+// softmax of tile i (scores S), overlapped with the QK^T of tile i+1 (keys
+// kn, scores Sn) and followed by O^T += V^T P^T of tile i.  MASKED tiles
+// exclude tokens at or beyond each row's end (erow) and drop the value
+// scale/zero of excluded tokens (their bytes may never have been written).
+template <int PRESET, int NQT, bool MASKED>
+__device__ inline void tile_step(const floatx16 (&S)[NQT], const ValRegs &vr, const KeyRegs<PRESET> &kn,
+                                 bool have_next, const _Float16 *qrow, floatx16 (&Sn)[NQT],
+                                 floatx16 (&acc)[4][NQT], SoftState<NQT> &st, const int (&erow)[NQT],
+                                 int tok0, int h)
+{
+    // 1. scores relative to the running max, the tile max, lazy rescale
+    float y[NQT][16];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const float msub = (st.m[qt] == -__builtin_inff()) ? 0.0f : st.m[qt];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const uint32_t w = vr.kf[v >> 3][(v & 7) >> 1];
+            const float kf = (v & 1) ? half_hi(w) : half_lo(w);
+            y[qt][v] = __builtin_fmaf(S[qt][v], kf, -msub);
+            if constexpr (MASKED) {
+                const int t = tok0 + 16 * (v >> 3) + 8 * h + (v & 7);
+                if (t >= erow[qt])
+                    y[qt][v] = -__builtin_inff();
+            }
+        }
+        float tmax = fmaxf(fmaxf(y[qt][0], y[qt][1]), y[qt][2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2)
+            tmax = fmaxf(fmaxf(tmax, y[qt][v]), y[qt][v + 1]);
+        tmax = fmaxf(tmax, y[qt][15]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const bool first = (st.m[qt] == -__builtin_inff());
+        const bool grow = first ? (tmax > -__builtin_inff()) : (tmax > kRescaleSlack);
+        if (__builtin_expect(__any(grow), 0)) { // rare after the first tile
+            // rows that grew (or any row, for uniformity) move their max up
+            const float delta = first ? ((tmax > -__builtin_inff()) ? tmax : 0.0f) : fmaxf(tmax, 0.0f);
+            if (!first || tmax > -__builtin_inff()) {
+                if (!first) {
+                    const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+                        acc[dt][qt] *= alpha;
+                    st.l[qt] *= alpha;
+                    st.z[qt] *= alpha;
+                }
+                st.m[qt] = msub + delta;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    y[qt][v] -= delta;
+            }
+        }
+    }
+
+    // 2. QK^T of the next tile (independent of the rest of this step)
+    if (have_next)
+        qk_tile<PRESET, NQT>(kn, qrow, Sn);
+
+    // 3. probabilities, their sums and the P operand
+    H8 Pb[NQT][2];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int v = 8 * s + 2 * j;
+                const float p0 = __builtin_amdgcn_exp2f(y[qt][v]);
+                const float p1 = __builtin_amdgcn_exp2f(y[qt][v + 1]);
+                const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
+                uint32_t vs = vr.vs[s][j], vz = vr.vz[s][j];
+                if constexpr (MASKED) {
+                    const int t = tok0 + 16 * s + 8 * h + 2 * j;
+                    const uint32_t keep = ((t < erow[qt]) ? 0x0000FFFFu : 0u) | ((t + 1 < erow[qt]) ? 0xFFFF0000u : 0u);
+                    vs &= keep;
+                    vz &= keep;
+                }
+                st.l[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, st.l[qt], false);
+                st.z[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vz), st.z[qt], false);
+                Pb[qt][s].u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vs));
+            }
+
+    // 4. O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const half8_t A = value_operand(vr, dt, s);
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+                acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pb[qt][s].h, acc[dt][qt], 0, 0, 0);
+        }
+}
+
+// Query preparation, once per (b, hk) unit: row r = n * G + g of the unit
+// is query head hk * G + g of speculative token n, scaled by sm_scale *
+// log2(e) (the softmax runs in base 2) and, for k3v4_nc, rotated by the same
+// normalised Walsh-Hadamard transform as the keys (q' = H q / sqrt(128)),
+// then rounded to binary16 -- the B operand of the QK^T MFMAs.  One
+// wavefront per row; lane l holds coordinates l and l + 64.
+__global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6); // unit * rows_pad + r
+    const int unit = row / a.rows_pad, rr = row % a.rows_pad;
+    const int b = unit / a.Hk, hk = unit % a.Hk;
+    float x0 = 0.0f, x1 = 0.0f;
+    if (rr < a.R) {
+        const int n = rr / a.G, g = rr % a.G;
+        const size_t off = ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
+        if (a.q_f16) {
+            const _Float16 *q = reinterpret_cast<const _Float16 *>(a.Q) + off;
+            x0 = (float)q[lane];
+            x1 = (float)q[lane + 64];
+        } else {
+            const float *q = reinterpret_cast<const float *>(a.Q) + off;
+            x0 = q[lane];
+            x1 = q[lane + 64];
+        }
+    }
+    float sc = a.qscale;
+    if (a.rotate) {
+#pragma unroll
+        for (int hh = 1; hh < 64; hh <<= 1) {
+            const float p0 = __shfl_xor(x0, hh, 64), p1 = __shfl_xor(x1, hh, 64);
+            x0 = (lane & hh) ? p0 - x0 : x0 + p0;
+            x1 = (lane & hh) ? p1 - x1 : x1 + p1;
+        }
+        const float u = x0, v = x1;
+        x0 = u + v;
+        x1 = u - v;
+        sc *= 0.08838834764831845f; // 1 / sqrt(128)
+    }
+    _Float16 *dst = a.qp + (size_t)row * kQPadHalfs;
+    dst[lane] = (_Float16)(x0 * sc);
+    dst[lane + 64] = (_Float16)(x1 * sc);
+    if (lane < kQPadHalfs - kD)
+        dst[kD + lane] = (_Float16)0.0f;
+}
+
 template <int PRESET, int NQT>
 __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
 {
     constexpr int RP = 32 * NQT; // padded rows
     constexpr int LPT = Ring<PRESET>::kLoads, DEPTH = Ring<PRESET>::kDepth;
     constexpr int kSlotBytes = LPT * 1024;
-    // query region: raw rows (up to fp32, 512 B each) while they arrive, then
-    // the scaled/rotated fp16 rows the MFMA B operands are read from
-    constexpr int kQBytes = RP * 512;
-    static_assert(RP * kQStride * 2 <= kQBytes, "query staging");
+    // query region: the unit's prepared fp16 rows (RP x kQPadHalfs), copied
+    // in 1 KiB loads into a region rounded up to whole KiB
+    constexpr int kQBytes = RP * kQPadHalfs * 2;
+    constexpr int kQRegion = (kQBytes + 1023) / 1024 * 1024;
     constexpr int kRingBytes = kWaves * DEPTH * kSlotBytes;
     constexpr int kMergeBytes = (kWaves * RP * kAccStride + kWaves * RP * 4 + RP * 3) * 4;
-    constexpr int kLdsBytes = (kQBytes + kRingBytes) > kMergeBytes ? (kQBytes + kRingBytes) : kMergeBytes;
+    constexpr int kLdsBytes = (kQRegion + kRingBytes) > kMergeBytes ? (kQRegion + kRingBytes) : kMergeBytes;
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
@@ -311,86 +498,25 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
     using L_ = Layout<PRESET>;
     const uint8_t *ubase = a.base + (size_t)unit * a.nblk * L_::kBlockBytes;
     _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
-    uint8_t *ring = lds + kQBytes + wave * DEPTH * kSlotBytes;
+    uint8_t *ring = lds + kQRegion + wave * DEPTH * kSlotBytes;
 
     // ------------------------------------------------------------ prologue
-    // The query rows of this unit and the first ring tiles are all fetched
-    // with direct global->LDS loads, query first: waiting for the query then
-    // means "all but the ring prefill", so the query scaling / rotation runs
-    // while the key/value tiles are still arriving.
-    const int qes = a.q_f16 ? 2 : 4;          // bytes per query element
-    const int qrow = kD * qes;                // bytes per query row
+    // The unit's prepared query rows (qprep_kernel) and the first ring tiles
+    // arrive by direct global->LDS loads, query first, so that waiting for
+    // the query means "all but the ring prefill".
     {
-        const int qloads = (a.R * qrow + 1023) / 1024;
+        constexpr int kQLoads = kQRegion / 1024;
+        const uint8_t *qsrc = reinterpret_cast<const uint8_t *>(a.qp) + (size_t)unit * kQBytes;
         const uint32_t qlds = (uint32_t)(size_t)(lds_void_t *)lds;
-        const uint8_t *Qb = reinterpret_cast<const uint8_t *>(a.Q);
-        for (int J = wave; J < qloads; J += kWaves) {
-            const int o = 1024 * J + 16 * lane;
-            int r = o / qrow;
-            const int within = o - r * qrow;
-            r = r < a.R ? r : 0; // padding lanes re-read row 0 (ignored)
-            const int n = r / a.G, g = r % a.G;
-            dma16(Qb + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * qrow + within, qlds + 1024 * J);
-        }
+        for (int J = wave; J < kQLoads; J += kWaves)
+            dma16(qsrc + min(1024 * J + 16 * lane, kQBytes - 16), qlds + 1024 * J);
     }
     const int npre = min(DEPTH, ntile);
     for (int i = 0; i < npre; ++i)
         issue_tile<PRESET>(ubase, kt0 + i, a.nblk, ring + i * kSlotBytes, lane);
     wait_ring<LPT>(npre);          // this wavefront's query loads are done
     __builtin_amdgcn_s_barrier();  // ... and every other wavefront's
-
-    constexpr int kRowsPerWave = RP / kWaves;
-    _Float16 qh[kRowsPerWave][2];
-#pragma unroll
-    for (int j = 0; j < kRowsPerWave; ++j) {
-        const int rr = wave + kWaves * j;
-        float x0 = 0.0f, x1 = 0.0f;
-        if (rr < a.R) {
-            if (a.q_f16) {
-                const _Float16 *q = reinterpret_cast<const _Float16 *>(lds + rr * qrow);
-                x0 = (float)q[lane];
-                x1 = (float)q[lane + 64];
-            } else {
-                const float *q = reinterpret_cast<const float *>(lds + rr * qrow);
-                x0 = q[lane];
-                x1 = q[lane + 64];
-            }
-        }
-        if constexpr (PRESET == kPresetK3V4) {
-            // q' = H q / sqrt(128): the keys live in the rotated space
-#pragma unroll
-            for (int hh = 1; hh < 64; hh <<= 1) {
-                float p0 = __shfl_xor(x0, hh, 64), p1 = __shfl_xor(x1, hh, 64);
-                x0 = (lane & hh) ? p0 - x0 : x0 + p0;
-                x1 = (lane & hh) ? p1 - x1 : x1 + p1;
-            }
-            const float u = x0, v = x1;
-            const float sc = a.qscale * 0.08838834764831845f;
-            x0 = (u + v) * sc;
-            x1 = (u - v) * sc;
-        } else {
-            x0 *= a.qscale;
-            x1 *= a.qscale;
-        }
-        qh[j][0] = (_Float16)x0;
-        qh[j][1] = (_Float16)x1;
-    }
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier(); // raw rows consumed: the region is rewritten below
-#pragma unroll
-    for (int j = 0; j < kRowsPerWave; ++j) {
-        const int rr = wave + kWaves * j;
-        qs[rr * kQStride + lane] = qh[j][0];
-        qs[rr * kQStride + lane + 64] = qh[j][1];
-    }
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    half8_t qB[NQT][8];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qB[qt][ks] = *reinterpret_cast<const half8_t *>(qs + (32 * qt + col) * kQStride + 64 * h + 8 * ks);
+    const _Float16 *qlane = qs + col * kQStride + 64 * h; // this lane's B-operand row
 
     // Effective end of this lane's query rows (causal window of the pages).
     int erow[NQT];
@@ -408,119 +534,58 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
             acc[dt][qt] = floatx16{0};
-    float mrow[NQT], lsum[NQT], zsum[NQT];
+    SoftState<NQT> st;
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        mrow[qt] = -__builtin_inff();
-        lsum[qt] = 0.0f;
-        zsum[qt] = 0.0f;
+        st.m[qt] = -__builtin_inff();
+        st.l[qt] = 0.0f;
+        st.z[qt] = 0.0f;
     }
 
-    for (int i = 0; i < ntile; ++i) {
+    // Software pipeline: the scores of tile i+1 are computed while tile i's
+    // softmax and P*V run.  Slot i is refilled with tile i + DEPTH once both
+    // of its halves have been read (keys one iteration earlier).
+    floatx16 S[NQT], Sn[NQT];
+    if (ntile > 0) {
+        wait_ring<LPT>(min(ntile - 1, DEPTH - 1));
+        KeyRegs<PRESET> k0;
+        read_keys<PRESET>(k0, ring, lane);
+        qk_tile<PRESET, NQT>(k0, qlane, S);
+    }
+    // tiles [0, nfast) need no masking; the rest (the sequence's last tile
+    // and the causal window) run in a separate, identical loop so that the
+    // masking code does not share the main loop's registers
+    const int nfast = max(0, min(ntile, (emin - kt0 * kTile) / kTile));
+    auto step = [&](int i, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int kt = kt0 + i;
         uint8_t *slot = ring + (i % DEPTH) * kSlotBytes;
-        wait_ring<LPT>(min(ntile - 1 - i, DEPTH - 1));
-        Tile<PRESET> cur;
-        read_tile<PRESET>(cur, slot, lane);
+        ValRegs vr;
+        read_values<PRESET>(vr, slot, lane);
+        const bool have_next = i + 1 < ntile;
+        KeyRegs<PRESET> kn;
+        if (have_next) {
+            wait_ring<LPT>(min(ntile - i - 2, DEPTH - 2));
+            read_keys<PRESET>(kn, ring + ((i + 1) % DEPTH) * kSlotBytes, lane);
+        }
         wait_lgkm0();
         if (i + DEPTH < ntile)
             issue_tile<PRESET>(ubase, kt + DEPTH, a.nblk, slot, lane);
-
-        // S^T = K Q^T (32 tokens x RP rows)
-        floatx16 S[NQT];
+        tile_step<PRESET, NQT, MASKED>(S, vr, kn, have_next, qlane, Sn, acc, st, erow, kt * kTile, h);
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
-            S[qt] = floatx16{0};
+            S[qt] = Sn[qt];
+    };
+    for (int i = 0; i < nfast; ++i)
+        step(i, std::false_type{});
+    for (int i = nfast; i < ntile; ++i)
+        step(i, std::true_type{});
+    float mrow[NQT], lsum[NQT], zsum[NQT];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const half8_t A = key_operand<PRESET>(cur, ks);
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt)
-                S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qB[qt][ks], S[qt], 0, 0, 0);
-        }
-
-        // per-token key factor of C register v: token 16(v/8) + 8h + v%8
-        float kf[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int s = v >> 3, u = v & 7;
-            if constexpr (PRESET == kPresetK3V4)
-                kf[v] = h2f(half_of(cur.m0[s], u)) * h2f(half_of(cur.m1[s], u));
-            else
-                kf[v] = h2f(half_of(cur.m0[s], u));
-        }
-        const int tok0 = kt * kTile;
-        const bool masked = tok0 + kTile > emin;
-
-        H8 Pb[NQT][2];
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            float x[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                x[v] = S[qt][v] * kf[v];
-            if (masked) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int t = tok0 + 16 * (v >> 3) + 8 * h + (v & 7);
-                    if (t >= erow[qt])
-                        x[v] = -__builtin_inff();
-                }
-            }
-            float tmax = x[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v)
-                tmax = fmaxf(tmax, x[v]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            if (__any(tmax > mrow[qt] + kRescaleSlack)) {
-                const float mnew = fmaxf(mrow[qt], tmax);
-                if (mrow[qt] != -__builtin_inff()) {
-                    const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
-                        acc[dt][qt] *= alpha;
-                    lsum[qt] *= alpha;
-                    zsum[qt] *= alpha;
-                }
-                mrow[qt] = mnew;
-            }
-            const float msub = (mrow[qt] == -__builtin_inff()) ? 0.0f : mrow[qt];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int v = 8 * s + 2 * j;
-                    const float p0 = __builtin_amdgcn_exp2f(x[v] - msub);
-                    const float p1 = __builtin_amdgcn_exp2f(x[v + 1] - msub);
-                    half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
-                    uint32_t vs = cur.vs[s][j], vz = cur.vz[s][j];
-                    if (masked) {
-                        // masked tokens may hold unwritten bytes: drop their
-                        // scale and zero so that 0 * garbage cannot appear
-                        const int t = tok0 + 16 * s + 8 * h + 2 * j;
-                        const uint32_t keep = ((t < erow[qt]) ? 0x0000FFFFu : 0u) |
-                                              ((t + 1 < erow[qt]) ? 0xFFFF0000u : 0u);
-                        vs &= keep;
-                        vz &= keep;
-                    }
-                    const half2_t vsh = __builtin_bit_cast(half2_t, vs);
-                    const half2_t vzh = __builtin_bit_cast(half2_t, vz);
-                    lsum[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, lsum[qt], false);
-                    zsum[qt] = __builtin_amdgcn_fdot2(ph, vzh, zsum[qt], false);
-                    Pb[qt][s].u[j] = __builtin_bit_cast(uint32_t, ph * vsh);
-                }
-        }
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const half8_t A = value_operand<PRESET>(cur, dt, s);
-#pragma unroll
-                for (int qt = 0; qt < NQT; ++qt)
-                    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pb[qt][s].h, acc[dt][qt], 0, 0, 0);
-            }
+    for (int qt = 0; qt < NQT; ++qt) {
+        mrow[qt] = st.m[qt];
+        lsum[qt] = st.l[qt];
+        zsum[qt] = st.z[qt];
     }
 
     // ---------------------------------------------------------------- merge
@@ -586,8 +651,9 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
             s4.w += al * x.w;
         }
         const float Ls = rstat[rr * 3 + 0], Zs = rstat[rr * 3 + 1];
-        // odd d carry the 16x high-nibble scale of the value operand
-        float4 o = make_float4(s4.x + Zs, s4.y * 0.0625f + Zs, s4.z + Zs, s4.w * 0.0625f + Zs);
+        // the value operand carried c * 2^-24 (even d) and 16c * 2^-24 (odd d)
+        float4 o = make_float4(s4.x * 16777216.0f + Zs, s4.y * 1048576.0f + Zs, s4.z * 16777216.0f + Zs,
+                               s4.w * 1048576.0f + Zs);
         // Ls == 0: the row saw no token in this range.  A NaN Ls (a NaN key
         // or scale the row can see) propagates to the output.
         if (a.nsplit == 1) {
@@ -605,70 +671,62 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
     }
 }
 
-// Merge of the key-range partitions of each (b, hk).  One block of 256
-// threads per (unit, 8 query rows): the (max, sum) pairs of all ranges are
-// staged in LDS once, then each thread merges one float4 of one row with all
-// of that row's partial loads in flight together.
-constexpr int kCombineRows = 8;
+// Merge of the key-range partitions of each (b, hk): out = sum_s w_s O_s /
+// sum_s w_s with w_s = exp2(m_s - max_s m_s) * l_s.  One 32-lane group per
+// (unit, row), one float4 of the row per lane; every lane loads the row's
+// (m, l) pairs and its own partial float4s in one batch, so the kernel costs
+// a single round trip to memory.  Ranges whose softmax sum is exactly 0 saw
+// no token and get weight 0; a NaN sum is kept so that it reaches the output.
 constexpr int kCombineChunk = 16;
-constexpr int kCombineMaxSplits = 256;
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 {
-    __shared__ float wts[kCombineRows][kCombineMaxSplits];
-    __shared__ float sums[kCombineRows][kCombineMaxSplits];
-    __shared__ float inv_den[kCombineRows];
-    const int groups = (a.R + kCombineRows - 1) / kCombineRows;
-    const int unit = blockIdx.x / groups, r0 = (blockIdx.x % groups) * kCombineRows;
-    const size_t base = (size_t)unit * a.nsplit * a.R;
-    // ranges whose softmax sum is exactly 0 saw no token (weight 0); a NaN
-    // sum is kept so that it reaches the output
-    for (int e = threadIdx.x; e < kCombineRows * a.nsplit; e += 256) {
-        const int rl = e / a.nsplit, sp = e % a.nsplit;
-        float2 ml = make_float2(-__builtin_inff(), 0.0f);
-        if (r0 + rl < a.R)
-            ml = a.part_ml[base + (size_t)sp * a.R + r0 + rl];
-        wts[rl][sp] = (ml.y != 0.0f) ? ml.x : -__builtin_inff();
-        sums[rl][sp] = ml.y;
-    }
-    __syncthreads();
-    if (threadIdx.x < kCombineRows) {
-        const int rl = threadIdx.x;
-        float M = -__builtin_inff();
-        for (int sp = 0; sp < a.nsplit; ++sp)
-            M = fmaxf(M, wts[rl][sp]);
-        float den = 0.0f;
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            const float l = sums[rl][sp];
-            const float w = (l != 0.0f) ? __builtin_amdgcn_exp2f(wts[rl][sp] - M) * l : 0.0f;
-            wts[rl][sp] = w;
-            den += w;
-        }
-        inv_den[rl] = (den != 0.0f) ? 1.0f / den : __builtin_nanf("");
-    }
-    __syncthreads();
-    const int rl = threadIdx.x >> 5, d = (threadIdx.x & 31) * 4;
-    const int rr = r0 + rl;
-    if (rr >= a.R)
+    const int grp = blockIdx.x * 8 + (threadIdx.x >> 5);
+    if (grp >= a.B * a.Hk * a.R)
         return;
+    const int unit = grp / a.R, rr = grp % a.R;
+    const int d = (threadIdx.x & 31) * 4;
+    const size_t base = (size_t)unit * a.nsplit * a.R + rr;
+    float M = -__builtin_inff(), den = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < a.nsplit; s0 += kCombineChunk) {
+        float2 ml[kCombineChunk];
         float4 v[kCombineChunk];
 #pragma unroll
-        for (int j = 0; j < kCombineChunk; ++j)
-            if (s0 + j < a.nsplit)
-                v[j] = *reinterpret_cast<const float4 *>(a.part_o + (base + (size_t)(s0 + j) * a.R + rr) * kD + d);
+        for (int j = 0; j < kCombineChunk; ++j) {
+            if (s0 + j < a.nsplit) {
+                const size_t ix = base + (size_t)(s0 + j) * a.R;
+                ml[j] = a.part_ml[ix];
+                v[j] = *reinterpret_cast<const float4 *>(a.part_o + ix * kD + d);
+            } else {
+                ml[j] = make_float2(-__builtin_inff(), 0.0f);
+                v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float Mc = M;
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j)
-            if (s0 + j < a.nsplit) {
-                const float w = wts[rl][s0 + j];
-                acc.x += w * v[j].x;
-                acc.y += w * v[j].y;
-                acc.z += w * v[j].z;
-                acc.w += w * v[j].w;
-            }
+            if (ml[j].y != 0.0f)
+                Mc = fmaxf(Mc, ml[j].x);
+        // rescale what earlier chunks accumulated to the new maximum
+        const float r = (M == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+        den *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+        M = Mc;
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j) {
+            const float w = (ml[j].y != 0.0f) ? __builtin_amdgcn_exp2f(ml[j].x - M) * ml[j].y : 0.0f;
+            den += w;
+            acc.x += w * v[j].x;
+            acc.y += w * v[j].y;
+            acc.z += w * v[j].z;
+            acc.w += w * v[j].w;
+        }
     }
-    const float inv = inv_den[rl];
+    const float inv = (den != 0.0f) ? 1.0f / den : __builtin_nanf("");
     const int b = unit / a.Hk, hk = unit % a.Hk;
     const int n = rr / a.G, g = rr % a.G;
     *reinterpret_cast<float4 *>(a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD + d) =
@@ -694,9 +752,16 @@ hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s
     return hipGetLastError();
 }
 
+hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(a.B * a.Hk * a.rows_pad / 4)), block(256);
+    hipLaunchKernelGGL(qprep_kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.B * a.Hk * ((a.R + kCombineRows - 1) / kCombineRows))), block(256);
+    const dim3 grid((unsigned)((a.B * a.Hk * a.R + 7) / 8)), block(256);
     hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, a);
     return hipGetLastError();
 }
