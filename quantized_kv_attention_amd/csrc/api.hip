@@ -83,24 +83,14 @@ int check_verify_shape(const tqkv_cache *c, int n_spec, int Hq)
     return TQKV_OK;
 }
 
-// Workspace: the prepared query operands of every unit, then (with more
-// than one key range) the normalised partial outputs and their (max, sum).
-size_t qprep_bytes(const tqkv_cache *c, int n_spec, int Hq)
-{
-    const int R = (Hq / c->Hk) * n_spec;
-    const int rows_pad = R <= 32 ? 32 : 64;
-    const size_t b = (size_t)c->B * c->Hk * rows_pad * kQPadHalfs * 2;
-    return (b + 255) / 256 * 256;
-}
-
+// Workspace: with more than one key range, the normalised partial outputs
+// and their (max, sum); nothing otherwise.
 size_t workspace_for(const tqkv_cache *c, int n_spec, int Hq, int splits)
 {
-    size_t total = qprep_bytes(c, n_spec, Hq);
-    if (splits > 1) {
-        const size_t rows = (size_t)c->B * c->Hk * splits * (size_t)((Hq / c->Hk) * n_spec);
-        total += rows * TQKV_HEAD_DIM * sizeof(float) + rows * 2 * sizeof(float);
-    }
-    return total;
+    if (splits <= 1)
+        return 0;
+    const size_t rows = (size_t)c->B * c->Hk * splits * (size_t)((Hq / c->Hk) * n_spec);
+    return rows * TQKV_HEAD_DIM * sizeof(float) + rows * 2 * sizeof(float);
 }
 
 } // namespace
@@ -208,36 +198,26 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
         return cus;
     const int splits = plan_splits(cache, num_splits, cus);
     const size_t need = workspace_for(cache, n_spec, Hq, splits);
-    if (!workspace || workspace_bytes < need)
-        return TQKV_ERR_WORKSPACE;
-    if (!aligned(workspace, 256))
-        return TQKV_ERR_ALIGN;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return TQKV_ERR_WORKSPACE;
+        if (!aligned(workspace, 256))
+            return TQKV_ERR_ALIGN;
+    }
     const int G = Hq / cache->Hk;
     const int R = G * n_spec;
-    const int rows_pad = R <= 32 ? 32 : 64;
     const float scale = (sm_scale == 0.0f) ? 0.08838834764831845f : sm_scale;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    QPrepArgs qa;
-    qa.Q = Q;
-    qa.qp = reinterpret_cast<_Float16 *>(ws);
-    qa.q_f16 = (q_dtype == TQKV_Q_F16);
-    qa.B = cache->B;
-    qa.Hk = cache->Hk;
-    qa.Hq = Hq;
-    qa.G = G;
-    qa.R = R;
-    qa.rows_pad = rows_pad;
-    qa.rotate = (cache->preset == TQKV_K3V4_NC);
-    qa.qscale = scale * 1.4426950408889634f;
     VerifyArgs a;
     a.base = static_cast<const uint8_t *>(cache->base);
-    a.qp = qa.qp;
+    a.Q = Q;
     a.seq_lens = seq_lens;
     a.out = out;
     const size_t units_rows = (size_t)cache->B * cache->Hk * splits * R;
-    float *part = reinterpret_cast<float *>(ws + qprep_bytes(cache, n_spec, Hq));
+    float *part = static_cast<float *>(workspace);
     a.part_o = splits > 1 ? part : nullptr;
     a.part_ml = splits > 1 ? reinterpret_cast<float2 *>(part + units_rows * TQKV_HEAD_DIM) : nullptr;
+    a.qscale = scale * 1.4426950408889634f;
+    a.q_f16 = (q_dtype == TQKV_Q_F16);
     a.Hk = cache->Hk;
     a.max_seq = cache->max_seq;
     a.nblk = nblocks(cache->max_seq);
@@ -249,8 +229,6 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
     a.causal = causal;
     a.nsplit = splits;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_qprep(qa, s) != hipSuccess)
-        return TQKV_ERR_LAUNCH;
     if (launch_verify(cache->preset, R <= 32 ? 1 : 2, a, s) != hipSuccess)
         return TQKV_ERR_LAUNCH;
     if (splits > 1) {

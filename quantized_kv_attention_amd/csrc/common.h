@@ -59,25 +59,15 @@ struct StoreArgs {
     int B, Hk, max_seq, nblk, T;
 };
 
-// Query operands prepared once per (b, hk) unit: R padded to 32 * NQT rows of
-// kQPadHalfs binary16 values (128 + 8 padding; the padding keeps the MFMA
-// B-operand reads of 32 rows from colliding on LDS banks).
-constexpr int kQPadHalfs = 136;
-
-struct QPrepArgs {
-    const void *Q;
-    _Float16 *qp; // [units][32 * nqt][kQPadHalfs]
-    int q_f16, B, Hk, Hq, G, R, rows_pad, rotate;
-    float qscale;
-};
-
 struct VerifyArgs {
     const uint8_t *base;
-    const _Float16 *qp; // prepared query operands (see QPrepArgs)
+    const void *Q;   // [N, B, Hq, 128], fp32 or fp16 (q_f16)
     const int32_t *seq_lens;
     float *out;      // final output (nsplit == 1)
     float *part_o;   // [units * nsplit * R][128] normalised partial outputs
     float2 *part_ml; // [units * nsplit * R] (running max in log2 units, softmax sum)
+    float qscale;    // softmax scale * log2(e)
+    int q_f16;
     int Hk, max_seq, nblk;
     int B, N, Hq, G, R, causal, nsplit;
 };
@@ -91,7 +81,6 @@ struct CombineArgs {
 
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
-hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s);
 hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 

@@ -26,6 +26,10 @@
 //    the score column, the value scale multiplies P, the value zero enters
 //    through sum_t p_t * zero_t.  Value codes enter the MFMA as the binary16
 //    integers c (low nibble) and 16c (high nibble), built with one mask.
+//  * The query operands are prepared inside the kernel (scale, WHT rotation
+//    for k3v4_nc as one small MFMA product with a +-1 matrix, fp16) and held
+//    in registers for the whole key loop; the output accumulators live in
+//    AGPRs, which the MFMAs read and write directly.
 //  * The four wavefronts merge their softmax states through LDS; with more
 //    than one key range per unit a second kernel merges the ranges.
 #include "codebook.h"
@@ -43,8 +47,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;        // tokens per inner-loop step
 constexpr int kWaves = 4;        // wavefronts per work-group
-constexpr int kQStride = kQPadHalfs; // halfs per query row in LDS (128 + pad)
+constexpr int kQStride = 136;    // halfs per fp16 query row in LDS (128 + 8: no bank collisions
+                                 // between the 32 rows an MFMA operand read touches)
 constexpr int kAccStride = 132;  // floats per row of the LDS merge buffer
+constexpr int kInitTiles = 2;    // ring tiles issued before the query preparation
 
 union H8 {
     half8_t h;
@@ -56,15 +62,6 @@ __device__ inline float h2f(uint16_t h) { return __half2float(__ushort_as_half(h
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
     return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// 4 packed 3-bit codes (one per byte, values 0..7) -> 4 fp16 centroids
-__device__ inline void k3_lookup(uint32_t sel, uint32_t &out01, uint32_t &out23)
-{
-    const uint32_t lo = perm(kLoBytes47, kLoBytes03, sel);
-    const uint32_t hi = perm(kHiBytes47, kHiBytes03, sel);
-    out01 = perm(hi, lo, 0x05010400u);
-    out23 = perm(hi, lo, 0x07030602u);
 }
 
 // ---------------------------------------------------------------------------
@@ -114,16 +111,17 @@ template <int LPT> __device__ inline void wait_ring(int tiles)
     }
 }
 
-// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes at `g` land at
-// LDS byte lds_base + 16 * l.  Written as inline assembly so that the
-// compiler's wait insertion does not treat it as a pending write to every
-// LDS location (it would wait for the whole ring before each LDS read); the
-// ring's completion is tracked explicitly with wait_ring().  Inline memory
-// operations the compiler cannot see can only make its own waits longer,
-// never shorter, because loads complete in order.  M0 is not used by any
-// other instruction of this kernel.
+// 16-byte-per-lane global -> LDS loads: lane l's 16 bytes land at LDS byte
+// lds_base + 16 * l.  Written as inline assembly so that the compiler's wait
+// insertion does not treat them as pending writes to every LDS location (it
+// would wait for the whole ring before each LDS read); their completion is
+// tracked explicitly with wait_ring().  Inline memory operations the
+// compiler cannot see can only make its own waits longer, never shorter,
+// because loads complete in order.  M0 is not used by any other instruction
+// of this kernel.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// per-lane 64-bit address
 __device__ inline void dma16(const void *g, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -131,39 +129,79 @@ __device__ inline void dma16(const void *g, uint32_t lds_base)
                  : "v"(g), "s"(lds_base)
                  : "memory", "m0");
 }
+// wave-uniform base in SGPRs + per-lane 32-bit byte offset
+__device__ inline void dma16_s(const void *base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds_base)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// Issue the loads of tile kt (blocks 2kt, 2kt+1 of this unit) into `slot`.
-// Lanes past the last valid byte re-read the final 16 B (the unit's last
-// block exists; a missing second block is only ever masked).
+// Issue the loads of tile kt (blocks 2kt, 2kt+1 of this unit) into the
+// ring slot at LDS address slot_lds.  Load j covers tile bytes
+// [1024 j, 1024 j + 1024); the last load's lanes past the tile end re-read
+// its final 16 B (voff_last = min(16 lane, tile bytes - 16 - 1024 j)).  A
+// tile whose second block lies past the unit's last block (odd block count)
+// clamps every load to the first block; the missing half is only ever
+// masked.
 template <int PRESET>
-__device__ inline void issue_tile(const uint8_t *ubase, int kt, int nblk, uint8_t *slot, int lane)
+__device__ inline void issue_tile(const uint8_t *ubase, int kt, int nblk, uint32_t slot_lds, uint32_t voff,
+                                  uint32_t voff_last, int lane)
 {
     using L = Layout<PRESET>;
-    // the tile's bytes [0, valid); loads past the end re-read the final 16 B
-    const int valid = min(2, nblk - 2 * kt) * L::kBlockBytes;
+    constexpr int LPT = Ring<PRESET>::kLoads;
     const uint8_t *src = ubase + (size_t)(2 * kt) * L::kBlockBytes;
-    const uint32_t lds = (uint32_t)(size_t)(lds_void_t *)slot;
+    if (__builtin_expect(2 * kt + 1 < nblk, 1)) {
 #pragma unroll
-    for (int j = 0; j < Ring<PRESET>::kLoads; ++j) {
-        dma16(src + min(1024 * j + 16 * lane, valid - 16), lds + 1024 * j);
+        for (int j = 0; j < LPT - 1; ++j)
+            dma16_s(src + 1024 * j, voff, slot_lds + 1024 * j);
+        dma16_s(src + 1024 * (LPT - 1), voff_last, slot_lds + 1024 * (LPT - 1));
+    } else {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j)
+            dma16_s(src, (uint32_t)min(1024 * j + 16 * lane, L::kBlockBytes - 16), slot_lds + 1024 * j);
     }
 }
 
+// Maximum / sum of a per-lane value over the two lane halves (lanes l and
+// l ^ 32 hold the same query row): one v_permlane32_swap.
+__device__ inline void swap_halves(float x, float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ inline float halves_max(float x)
+{
+    float a, b;
+    swap_halves(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ inline float halves_sum(float x)
+{
+    float a, b;
+    swap_halves(x, a, b);
+    return a + b;
+}
+
 // Registers of one tile, read back from its ring slot: the key half (the A
-// operands of S^T = K Q^T) and the value half (value nibbles and per-token
-// fields), read at different times by the software pipeline below.
+// operands of S^T = K Q^T, with the token's key factor folded in) and the
+// value half (value nibbles and per-token scale/zero), read at different
+// times by the software pipeline below.
 template <int PRESET> struct KeyRegs;
 template <> struct KeyRegs<kPresetK3V4> {
-    uint2 k[3]; // 24 B: this lane's 64 key codes (two 32-code dword triples)
+    uint2 k[3];      // 24 B: this lane's 64 key codes (two 32-code dword triples)
+    uint32_t tab[4]; // byte tables of the 8 centroids times n*gamma: lo 0-3, lo 4-7, hi 0-3, hi 4-7
 };
 template <> struct KeyRegs<kPresetK8V4> {
-    u32x4 k[4]; // 64 B: this lane's 64 e4m3 key codes
+    u32x4 k[4];  // 64 B: this lane's 64 e4m3 key codes
+    uint32_t kf; // the token's key scale (fp16) in both halves
 };
 struct ValRegs {
-    u32x4 v[2];  // value nibbles of blocks 0/1 (8-token runs at 4 d's)
-    u32x4 kf[2]; // per-token key factor (fp16): n*gamma (k3v4_nc) or kscale (k8v4), tokens 8h..8h+7
-    u32x4 vs[2], vz[2];
+    u32x4 v[2];         // value nibbles of blocks 0/1 (8-token runs at 4 d's)
+    u32x4 vs[2], vz[2]; // value scale / zero (fp16) of the lane's tokens 16s + 8h + 0..7
 };
 
 // Token of the 32-token tile that MFMA row m stands for: bits 2 and 3 of m
@@ -175,27 +213,48 @@ __device__ inline int tile_token_of_row(int m)
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+__device__ inline uint32_t hmul2(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
+}
+
+// The lane's key codes and key factor.  The factor (the per-token key scale,
+// or n * gamma) multiplies the key operand instead of the score column: for
+// FP8 with one packed fp16 multiply per code pair (the scale operand of
+// v_cvt_scalef32_pk_f16_fp8 only applies a power of two), for the 3-bit
+// codes through a per-lane table of scaled centroids (4 multiplies + 4 byte
+// permutes per tile).
 template <int PRESET>
 __device__ inline void read_keys(KeyRegs<PRESET> &t, const uint8_t *slot, int lane)
 {
     using L = Layout<PRESET>;
     const int h = lane >> 5, m = lane & 31;
     const int tok = tile_token_of_row(m);
-    const uint8_t *kb = slot + (tok >> 4) * L::kBlockBytes + (tok & 15) * L::kKeyBytesPerToken;
+    const uint8_t *blk = slot + (tok >> 4) * L::kBlockBytes;
+    const uint8_t *kb = blk + (tok & 15) * L::kKeyBytesPerToken;
     if constexpr (PRESET == kPresetK3V4) {
 #pragma unroll
         for (int j = 0; j < 3; ++j)
             t.k[j] = *reinterpret_cast<const uint2 *>(kb + 24 * h + 8 * j);
+        const uint32_t n = *reinterpret_cast<const uint16_t *>(blk + L::kMeta0 + 2 * (tok & 15));
+        const uint32_t g = *reinterpret_cast<const uint16_t *>(blk + L::kMeta1 + 2 * (tok & 15));
+        const uint32_t f = hmul2(n, g);          // n * gamma in the low half
+        const uint32_t ff = f | (f << 16);       // ... in both halves
+        const uint32_t c01 = hmul2(kCentroidHalf[0] | ((uint32_t)kCentroidHalf[1] << 16), ff);
+        const uint32_t c23 = hmul2(kCentroidHalf[2] | ((uint32_t)kCentroidHalf[3] << 16), ff);
+        const uint32_t c45 = hmul2(kCentroidHalf[4] | ((uint32_t)kCentroidHalf[5] << 16), ff);
+        const uint32_t c67 = hmul2(kCentroidHalf[6] | ((uint32_t)kCentroidHalf[7] << 16), ff);
+        t.tab[0] = perm(c23, c01, 0x06040200u);
+        t.tab[1] = perm(c67, c45, 0x06040200u);
+        t.tab[2] = perm(c23, c01, 0x07050301u);
+        t.tab[3] = perm(c67, c45, 0x07050301u);
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             t.k[j] = *reinterpret_cast<const u32x4 *>(kb + 64 * h + 16 * j);
+        const uint32_t f = *reinterpret_cast<const uint16_t *>(blk + L::kMeta0 + 2 * (tok & 15));
+        t.kf = f | (f << 16);
     }
-}
-
-__device__ inline uint32_t hmul2(uint32_t a, uint32_t b)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
 }
 
 template <int PRESET>
@@ -207,29 +266,22 @@ __device__ inline void read_values(ValRegs &t, const uint8_t *slot, int lane)
     for (int s = 0; s < 2; ++s) {
         const uint8_t *bs = slot + s * L::kBlockBytes;
         t.v[s] = *reinterpret_cast<const u32x4 *>(bs + L::kValOff + (2 * m + h) * 16);
-        const u32x4 n = *reinterpret_cast<const u32x4 *>(bs + L::kMeta0 + 16 * h);
-        if constexpr (PRESET == kPresetK3V4) {
-            // n * gamma per token, as fp16 pairs (one v_pk_mul_f16 per pair).
-            // Written component by component: an in-place update of vector
-            // elements in a loop (kf[s][j] = f(kf[s][j], g[j])) was
-            // miscompiled by this toolchain (only g[0] was loaded).
-            const u32x4 g = *reinterpret_cast<const u32x4 *>(bs + L::kMeta1 + 16 * h);
-            u32x4 kf;
-            kf.x = hmul2(n.x, g.x);
-            kf.y = hmul2(n.y, g.y);
-            kf.z = hmul2(n.z, g.z);
-            kf.w = hmul2(n.w, g.w);
-            t.kf[s] = kf;
-        } else {
-            t.kf[s] = n;
-        }
         t.vs[s] = *reinterpret_cast<const u32x4 *>(bs + L::kVScale + 16 * h);
         t.vz[s] = *reinterpret_cast<const u32x4 *>(bs + L::kVZero + 16 * h);
     }
 }
 
+// 4 packed 3-bit codes (one per byte, values 0..7) -> 4 fp16 table entries
+__device__ inline void k3_lookup(const uint32_t (&tab)[4], uint32_t sel, uint32_t &out01, uint32_t &out23)
+{
+    const uint32_t lo = perm(tab[1], tab[0], sel);
+    const uint32_t hi = perm(tab[3], tab[2], sel);
+    out01 = perm(hi, lo, 0x05010400u);
+    out23 = perm(hi, lo, 0x07030602u);
+}
+
 // A operand of k-step ks of S^T = K Q^T: coordinates 64h + 8ks + 0..7 of
-// this lane's token.
+// this lane's token, times its key factor.
 template <int PRESET>
 __device__ inline half8_t key_operand(const KeyRegs<PRESET> &t, int ks)
 {
@@ -254,24 +306,27 @@ __device__ inline half8_t key_operand(const KeyRegs<PRESET> &t, int ks)
             sa = ((d0 >> 6) & 0x03030303u) | ((d2 >> 4) & 0x04040404u);
             sb = ((d1 >> 6) & 0x03030303u) | ((d2 >> 5) & 0x04040404u);
         }
-        k3_lookup(sa, o.u[0], o.u[1]);
-        k3_lookup(sb, o.u[2], o.u[3]);
+        k3_lookup(t.tab, sa, o.u[0], o.u[1]);
+        k3_lookup(t.tab, sb, o.u[2], o.u[3]);
     } else {
         const uint32_t a = t.k[ks >> 1][2 * (ks & 1)], b = t.k[ks >> 1][2 * (ks & 1) + 1];
-        half2_t x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false);
-        half2_t x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true);
-        half2_t x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
-        half2_t x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true);
-        o.h = half8_t{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+        const half2_t f = __builtin_bit_cast(half2_t, t.kf);
+        const half2_t x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false) * f;
+        const half2_t x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true) * f;
+        const half2_t x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false) * f;
+        const half2_t x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true) * f;
+        o.u[0] = __builtin_bit_cast(uint32_t, x0);
+        o.u[1] = __builtin_bit_cast(uint32_t, x1);
+        o.u[2] = __builtin_bit_cast(uint32_t, x2);
+        o.u[3] = __builtin_bit_cast(uint32_t, x3);
     }
     return o.h;
 }
 
-// S^T = K Q^T for one tile.  The query B operands are re-read from the LDS
-// query tile (qrow points at this lane's row and half) instead of being held
-// in 8*NQT*4 VGPRs across the whole loop.
+// S^T = K Q^T for one tile; QB[qt][ks] is the query B operand of k-step ks
+// (coordinates 64h + 8ks + 0..7 of this lane's query row 32qt + lane%32).
 template <int PRESET, int NQT>
-__device__ inline void qk_tile(const KeyRegs<PRESET> &k, const _Float16 *qrow, floatx16 (&S)[NQT])
+__device__ inline void qk_tile(const KeyRegs<PRESET> &k, const half8_t (&QB)[NQT][8], floatx16 (&S)[NQT])
 {
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
@@ -280,10 +335,8 @@ __device__ inline void qk_tile(const KeyRegs<PRESET> &k, const _Float16 *qrow, f
     for (int ks = 0; ks < 8; ++ks) {
         const half8_t A = key_operand<PRESET>(k, ks);
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            const half8_t Bq = *reinterpret_cast<const half8_t *>(qrow + 32 * qt * kQStride + 8 * ks);
-            S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bq, S[qt], 0, 0, 0);
-        }
+        for (int qt = 0; qt < NQT; ++qt)
+            S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, QB[qt][ks], S[qt], 0, 0, 0);
     }
 }
 
@@ -293,11 +346,11 @@ __device__ inline void qk_tile(const KeyRegs<PRESET> &k, const _Float16 *qrow, f
 // 16c * 2^-24 (gfx950's f16 MFMA multiplies subnormal inputs exactly), so
 // one mask per half-pair builds the operand; the epilogue rescales even d by
 // 2^24 and odd d by 2^20.
-__device__ inline half8_t value_operand(const ValRegs &t, int dt, int s)
+__device__ inline half8_t value_operand(const u32x4 (&v)[2], int dt, int s)
 {
     const int e = dt >> 1;
     const uint32_t mask = (dt & 1) ? 0x00F000F0u : 0x000F000Fu;
-    const uint32_t wa = t.v[s][2 * e], wb = t.v[s][2 * e + 1];
+    const uint32_t wa = v[s][2 * e], wb = v[s][2 * e + 1];
     H8 o;
     o.u[0] = wa & mask;
     o.u[1] = (wa >> 8) & mask;
@@ -305,9 +358,6 @@ __device__ inline half8_t value_operand(const ValRegs &t, int dt, int s)
     o.u[3] = (wb >> 8) & mask;
     return o.h;
 }
-
-__device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
-__device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
 
 // Lazy rescaling: the running row maximum m only moves when a tile's maximum
 // exceeds it by more than kRescaleSlack (log2 units), so probabilities are
@@ -320,144 +370,31 @@ template <int NQT> struct SoftState {
     float m[NQT], l[NQT], z[NQT];
 };
 
-// softmax of tile i (scores S), overlapped with the QK^T of tile i+1 (keys
-// kn, scores Sn) and followed by O^T += V^T P^T of tile i.  MASKED tiles
-// exclude tokens at or beyond each row's end (erow) and drop the value
-// scale/zero of excluded tokens (their bytes may never have been written).
-template <int PRESET, int NQT, bool MASKED>
-__device__ inline void tile_step(const floatx16 (&S)[NQT], const ValRegs &vr, const KeyRegs<PRESET> &kn,
-                                 bool have_next, const _Float16 *qrow, floatx16 (&Sn)[NQT],
-                                 floatx16 (&acc)[4][NQT], SoftState<NQT> &st, const int (&erow)[NQT],
-                                 int tok0, int h)
+// LDS barrier: the wavefront's LDS operations are complete before it
+// arrives, and no LDS access moves across it in either direction.  (The
+// ring's outstanding global->LDS loads are not waited for.)
+__device__ inline void lds_barrier()
 {
-    // 1. scores relative to the running max, the tile max, lazy rescale
-    float y[NQT][16];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        const float msub = (st.m[qt] == -__builtin_inff()) ? 0.0f : st.m[qt];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const uint32_t w = vr.kf[v >> 3][(v & 7) >> 1];
-            const float kf = (v & 1) ? half_hi(w) : half_lo(w);
-            y[qt][v] = __builtin_fmaf(S[qt][v], kf, -msub);
-            if constexpr (MASKED) {
-                const int t = tok0 + 16 * (v >> 3) + 8 * h + (v & 7);
-                if (t >= erow[qt])
-                    y[qt][v] = -__builtin_inff();
-            }
-        }
-        float tmax = fmaxf(fmaxf(y[qt][0], y[qt][1]), y[qt][2]);
-#pragma unroll
-        for (int v = 3; v < 15; v += 2)
-            tmax = fmaxf(fmaxf(tmax, y[qt][v]), y[qt][v + 1]);
-        tmax = fmaxf(tmax, y[qt][15]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const bool first = (st.m[qt] == -__builtin_inff());
-        const bool grow = first ? (tmax > -__builtin_inff()) : (tmax > kRescaleSlack);
-        if (__builtin_expect(__any(grow), 0)) { // rare after the first tile
-            // rows that grew (or any row, for uniformity) move their max up
-            const float delta = first ? ((tmax > -__builtin_inff()) ? tmax : 0.0f) : fmaxf(tmax, 0.0f);
-            if (!first || tmax > -__builtin_inff()) {
-                if (!first) {
-                    const float alpha = __builtin_amdgcn_exp2f(-delta);
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
-                        acc[dt][qt] *= alpha;
-                    st.l[qt] *= alpha;
-                    st.z[qt] *= alpha;
-                }
-                st.m[qt] = msub + delta;
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    y[qt][v] -= delta;
-            }
-        }
-    }
-
-    // 2. QK^T of the next tile (independent of the rest of this step)
-    if (have_next)
-        qk_tile<PRESET, NQT>(kn, qrow, Sn);
-
-    // 3. probabilities, their sums and the P operand
-    H8 Pb[NQT][2];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int v = 8 * s + 2 * j;
-                const float p0 = __builtin_amdgcn_exp2f(y[qt][v]);
-                const float p1 = __builtin_amdgcn_exp2f(y[qt][v + 1]);
-                const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
-                uint32_t vs = vr.vs[s][j], vz = vr.vz[s][j];
-                if constexpr (MASKED) {
-                    const int t = tok0 + 16 * s + 8 * h + 2 * j;
-                    const uint32_t keep = ((t < erow[qt]) ? 0x0000FFFFu : 0u) | ((t + 1 < erow[qt]) ? 0xFFFF0000u : 0u);
-                    vs &= keep;
-                    vz &= keep;
-                }
-                st.l[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, st.l[qt], false);
-                st.z[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vz), st.z[qt], false);
-                Pb[qt][s].u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vs));
-            }
-
-    // 4. O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const half8_t A = value_operand(vr, dt, s);
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt)
-                acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pb[qt][s].h, acc[dt][qt], 0, 0, 0);
-        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-// Query preparation, once per (b, hk) unit: row r = n * G + g of the unit
-// is query head hk * G + g of speculative token n, scaled by sm_scale *
-// log2(e) (the softmax runs in base 2) and, for k3v4_nc, rotated by the same
-// normalised Walsh-Hadamard transform as the keys (q' = H q / sqrt(128)),
-// then rounded to binary16 -- the B operand of the QK^T MFMAs.  One
-// wavefront per row; lane l holds coordinates l and l + 64.
-__global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a)
+// The binary16 +-1 entries H[o][16ks + 8h + j], j = 0..7, of the Sylvester
+// Hadamard matrix (H[i][k] = (-1)^popcount(i & k)) for output coordinate o:
+// the A operand of k-step ks of the query rotation.  The sign splits over
+// the disjoint bit ranges of 16ks + 8h and j.
+__device__ inline half8_t hadamard_operand(int o, int ks, int h)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6); // unit * rows_pad + r
-    const int unit = row / a.rows_pad, rr = row % a.rows_pad;
-    const int b = unit / a.Hk, hk = unit % a.Hk;
-    float x0 = 0.0f, x1 = 0.0f;
-    if (rr < a.R) {
-        const int n = rr / a.G, g = rr % a.G;
-        const size_t off = ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
-        if (a.q_f16) {
-            const _Float16 *q = reinterpret_cast<const _Float16 *>(a.Q) + off;
-            x0 = (float)q[lane];
-            x1 = (float)q[lane + 64];
-        } else {
-            const float *q = reinterpret_cast<const float *>(a.Q) + off;
-            x0 = q[lane];
-            x1 = q[lane + 64];
-        }
-    }
-    float sc = a.qscale;
-    if (a.rotate) {
+    const uint32_t flip = (__builtin_popcount(o & (16 * ks + 8 * h)) & 1) ? 0x80008000u : 0u;
+    H8 r;
 #pragma unroll
-        for (int hh = 1; hh < 64; hh <<= 1) {
-            const float p0 = __shfl_xor(x0, hh, 64), p1 = __shfl_xor(x1, hh, 64);
-            x0 = (lane & hh) ? p0 - x0 : x0 + p0;
-            x1 = (lane & hh) ? p1 - x1 : x1 + p1;
-        }
-        const float u = x0, v = x1;
-        x0 = u + v;
-        x1 = u - v;
-        sc *= 0.08838834764831845f; // 1 / sqrt(128)
+    for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t lo = (__builtin_popcount(o & (2 * jj)) & 1) ? 0xBC00u : 0x3C00u;
+        const uint32_t hi = (__builtin_popcount(o & (2 * jj + 1)) & 1) ? 0xBC00u : 0x3C00u;
+        r.u[jj] = (lo | (hi << 16)) ^ flip;
     }
-    _Float16 *dst = a.qp + (size_t)row * kQPadHalfs;
-    dst[lane] = (_Float16)(x0 * sc);
-    dst[lane + 64] = (_Float16)(x1 * sc);
-    if (lane < kQPadHalfs - kD)
-        dst[kD + lane] = (_Float16)0.0f;
+    return r.h;
 }
 
 template <int PRESET, int NQT>
@@ -466,10 +403,10 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
     constexpr int RP = 32 * NQT; // padded rows
     constexpr int LPT = Ring<PRESET>::kLoads, DEPTH = Ring<PRESET>::kDepth;
     constexpr int kSlotBytes = LPT * 1024;
-    // query region: the unit's prepared fp16 rows (RP x kQPadHalfs), copied
-    // in 1 KiB loads into a region rounded up to whole KiB
-    constexpr int kQBytes = RP * kQPadHalfs * 2;
-    constexpr int kQRegion = (kQBytes + 1023) / 1024 * 1024;
+    // query region: the unit's raw rows (fp32: 512 B, fp16: 256 B each),
+    // then, in place, the fp16 operand rows (kQStride halfs each)
+    constexpr int kQRegion = RP * kD * 4;
+    static_assert(RP * kQStride * 2 <= kQRegion, "query region");
     constexpr int kRingBytes = kWaves * DEPTH * kSlotBytes;
     constexpr int kMergeBytes = (kWaves * RP * kAccStride + kWaves * RP * 4 + RP * 3) * 4;
     constexpr int kLdsBytes = (kQRegion + kRingBytes) > kMergeBytes ? (kQRegion + kRingBytes) : kMergeBytes;
@@ -497,26 +434,136 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
 
     using L_ = Layout<PRESET>;
     const uint8_t *ubase = a.base + (size_t)unit * a.nblk * L_::kBlockBytes;
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t *)lds;
+    const uint32_t ring_lds = lds0 + kQRegion + wave * DEPTH * kSlotBytes;
+    const uint8_t *ring = lds + kQRegion + wave * DEPTH * kSlotBytes;
     _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
-    uint8_t *ring = lds + kQRegion + wave * DEPTH * kSlotBytes;
 
     // ------------------------------------------------------------ prologue
-    // The unit's prepared query rows (qprep_kernel) and the first ring tiles
-    // arrive by direct global->LDS loads, query first, so that waiting for
-    // the query means "all but the ring prefill".
+    // 1. The unit's raw query rows -> LDS, 1 KiB per load (2 fp32 or 4 fp16
+    //    rows).  Row r = n * G + g is query head hk * G + g of speculative
+    //    token n; padding rows re-read row 0 and are zeroed below.  Every
+    //    wavefront queues these loads before any wavefront queues ring loads,
+    //    so the query does not wait behind the key stream.
     {
-        constexpr int kQLoads = kQRegion / 1024;
-        const uint8_t *qsrc = reinterpret_cast<const uint8_t *>(a.qp) + (size_t)unit * kQBytes;
-        const uint32_t qlds = (uint32_t)(size_t)(lds_void_t *)lds;
-        for (int J = wave; J < kQLoads; J += kWaves)
-            dma16(qsrc + min(1024 * J + 16 * lane, kQBytes - 16), qlds + 1024 * J);
+        const int esz = a.q_f16 ? 2 : 4;
+        const int rshift = a.q_f16 ? 4 : 5; // lanes per row: 16 or 32
+        const int rpi = 64 >> rshift;       // rows per load
+        const int rsub = lane >> rshift, cb = 16 * (lane & ((1 << rshift) - 1));
+        for (int J = wave; J < RP / rpi; J += kWaves) {
+            const int r = J * rpi + rsub;
+            const int rs = r < a.R ? r : 0;
+            const int n = rs / a.G, g = rs % a.G;
+            const uint8_t *src = static_cast<const uint8_t *>(a.Q) +
+                                 ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD * esz + cb;
+            dma16(src, lds0 + 1024 * J);
+        }
     }
-    const int npre = min(DEPTH, ntile);
-    for (int i = 0; i < npre; ++i)
-        issue_tile<PRESET>(ubase, kt0 + i, a.nblk, ring + i * kSlotBytes, lane);
-    wait_ring<LPT>(npre);          // this wavefront's query loads are done
-    __builtin_amdgcn_s_barrier();  // ... and every other wavefront's
-    const _Float16 *qlane = qs + col * kQStride + 64 * h; // this lane's B-operand row
+    __builtin_amdgcn_s_barrier();
+
+    // 2. the first ring tiles.  The ring fills progressively (at most two
+    //    tiles per step): a load instruction waits at issue while the memory
+    //    pipeline is full, so a deep prefill would hold the wavefront long
+    //    before any tile could be processed.
+    const uint32_t voff = 16 * lane;
+    const uint32_t voff_last = (uint32_t)min(16 * lane, 2 * L_::kBlockBytes - 16 - 1024 * (LPT - 1));
+    int issued = 0; // tiles of this wavefront issued so far (wave-uniform)
+    for (; issued < min(kInitTiles, ntile); ++issued)
+        issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + issued * kSlotBytes, voff, voff_last, lane);
+    wait_ring<LPT>(issued); // this wavefront's query loads have landed
+    lds_barrier();        // ... and every other wavefront's
+
+    // 3. scale (softmax scale * log2 e: the softmax runs in base 2) and round
+    //    to binary16; thread t converts CPT coordinates of row t / TPR
+    constexpr int CPT = 16 * NQT, TPR = kD / CPT;
+    {
+        const int rr = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * CPT;
+        uint32_t qh[CPT / 2];
+        if (a.q_f16) {
+            const _Float16 *src = reinterpret_cast<const _Float16 *>(lds + rr * 256) + c0;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 8) {
+                const half8_t x = *reinterpret_cast<const half8_t *>(src + c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const half2_t p = half2_t{(_Float16)((float)x[2 * j] * a.qscale),
+                                              (_Float16)((float)x[2 * j + 1] * a.qscale)};
+                    qh[c / 2 + j] = __builtin_bit_cast(uint32_t, p);
+                }
+            }
+        } else {
+            const float *src = reinterpret_cast<const float *>(lds + rr * 512) + c0;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + c);
+                qh[c / 2] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale)});
+                qh[c / 2 + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale)});
+            }
+        }
+        if (rr >= a.R) {
+#pragma unroll
+            for (int j = 0; j < CPT / 2; ++j)
+                qh[j] = 0u;
+        }
+        lds_barrier(); // every raw row has been read before it is overwritten
+        uint32_t *dst = reinterpret_cast<uint32_t *>(qs + rr * kQStride + c0);
+#pragma unroll
+        for (int j = 0; j < CPT / 2; j += 4)
+            *reinterpret_cast<u32x4 *>(dst + j) = u32x4{qh[j], qh[j + 1], qh[j + 2], qh[j + 3]};
+        lds_barrier();
+    }
+
+    // 4. k3v4_nc: rotate by the normalised WHT, q' = H q / sqrt(128), as the
+    //    MFMA product Q'^T = H Q^T; wavefront w computes output coordinates
+    //    32w..32w+31 of every row and writes them back in place
+    if constexpr (PRESET == kPresetK3V4) {
+        half8_t Bq[NQT][8];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                Bq[qt][ks] = *reinterpret_cast<const half8_t *>(qs + (32 * qt + col) * kQStride + 16 * ks + 8 * h);
+        floatx16 C[NQT];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+            C[qt] = floatx16{0};
+        const int o = 32 * wave + col;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const half8_t A = hadamard_operand(o, ks, h);
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+                C[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bq[qt][ks], C[qt], 0, 0, 0);
+        }
+        lds_barrier(); // every wavefront has read the unrotated rows
+        constexpr float kInvSqrt128 = 0.08838834764831845f;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // C register 4g + i is output coordinate 32w + 8g + 4h + i of row 32qt + col
+                const half2_t p0 = half2_t{(_Float16)(C[qt][4 * g] * kInvSqrt128), (_Float16)(C[qt][4 * g + 1] * kInvSqrt128)};
+                const half2_t p1 = half2_t{(_Float16)(C[qt][4 * g + 2] * kInvSqrt128), (_Float16)(C[qt][4 * g + 3] * kInvSqrt128)};
+                *reinterpret_cast<uint2 *>(qs + (32 * qt + col) * kQStride + 32 * wave + 8 * g + 4 * h) =
+                    make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+            }
+        lds_barrier();
+    }
+
+    // 5. the QK^T B operands, held in registers for the whole key loop
+    half8_t QB[NQT][8];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            QB[qt][ks] = *reinterpret_cast<const half8_t *>(qs + (32 * qt + col) * kQStride + 64 * h + 8 * ks);
+    // kept in AGPRs (MFMA reads its A/B operands from either register file),
+    // which leaves the VGPRs to the accumulators and the softmax
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            asm volatile("" : "+a"(QB[qt][ks]));
 
     // Effective end of this lane's query rows (causal window of the pages).
     int erow[NQT];
@@ -542,60 +589,190 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
         st.z[qt] = 0.0f;
     }
 
-    // Software pipeline: the scores of tile i+1 are computed while tile i's
-    // softmax and P*V run.  Slot i is refilled with tile i + DEPTH once both
-    // of its halves have been read (keys one iteration earlier).
-    floatx16 S[NQT], Sn[NQT];
+    // Software pipeline over the wavefront's tiles.  Step i takes the scores
+    // S_i (computed one step earlier) and
+    //   1. adds P_{i-1} V_{i-1} to the accumulators (MFMA) while it finds the
+    //      tile maximum of S_i (VALU), then rescales if a row maximum grew;
+    //   2. computes S_{i+1} = K_{i+1} Q^T (MFMA) while it turns S_i into the
+    //      probabilities P_i and their sums (VALU);
+    //   3. refills the ring.
+    // Two score buffers alternate between the steps.
+    floatx16 SA[NQT], SB[NQT];
+    H8 Pp[NQT][2]; // P operand of the previous tile (zero before the first)
+    u32x4 Vp[2];   // value nibbles of the previous tile
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            Pp[qt][s].h = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    Vp[0] = u32x4{0, 0, 0, 0};
+    Vp[1] = u32x4{0, 0, 0, 0};
     if (ntile > 0) {
-        wait_ring<LPT>(min(ntile - 1, DEPTH - 1));
+        wait_ring<LPT>(issued - 1);
         KeyRegs<PRESET> k0;
         read_keys<PRESET>(k0, ring, lane);
-        qk_tile<PRESET, NQT>(k0, qlane, S);
+        qk_tile<PRESET, NQT>(k0, QB, SA);
     }
     // tiles [0, nfast) need no masking; the rest (the sequence's last tile
-    // and the causal window) run in a separate, identical loop so that the
-    // masking code does not share the main loop's registers
+    // and the causal window) run in a separate loop
     const int nfast = max(0, min(ntile, (emin - kt0 * kTile) / kTile));
-    auto step = [&](int i, auto masked_tag) {
+    auto step = [&](int i, floatx16(&S)[NQT], floatx16(&Sn)[NQT], auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int kt = kt0 + i;
-        uint8_t *slot = ring + (i % DEPTH) * kSlotBytes;
-        ValRegs vr;
-        read_values<PRESET>(vr, slot, lane);
-        const bool have_next = i + 1 < ntile;
-        KeyRegs<PRESET> kn;
-        if (have_next) {
-            wait_ring<LPT>(min(ntile - i - 2, DEPTH - 2));
-            read_keys<PRESET>(kn, ring + ((i + 1) % DEPTH) * kSlotBytes, lane);
+        const int tok0 = kt * kTile;
+        // this tile's value fields and the next tile's keys (the last step
+        // re-reads its own keys; that product is never used)
+        int inext = i;
+        if (i + 1 < ntile) {
+            wait_ring<LPT>(issued - i - 2);
+            inext = i + 1;
         }
-        wait_lgkm0();
-        if (i + DEPTH < ntile)
-            issue_tile<PRESET>(ubase, kt + DEPTH, a.nblk, slot, lane);
-        tile_step<PRESET, NQT, MASKED>(S, vr, kn, have_next, qlane, Sn, acc, st, erow, kt * kTile, h);
+        ValRegs vr;
+        read_values<PRESET>(vr, ring + (i % DEPTH) * kSlotBytes, lane);
+        KeyRegs<PRESET> kn;
+        read_keys<PRESET>(kn, ring + (inext % DEPTH) * kSlotBytes, lane);
+
+        // 1. O^T += V_{i-1}^T P_{i-1}^T; tile maximum of S_i; lazy rescale
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const half8_t A = value_operand(Vp, dt, s);
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt)
+                    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pp[qt][s].h, acc[dt][qt], 0, 0, 0);
+            }
+        float tmax[NQT];
+        bool grow_any = false;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            if constexpr (MASKED) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (tok0 + 16 * (v >> 3) + 8 * h + (v & 7) >= erow[qt])
+                        S[qt][v] = -__builtin_inff();
+            }
+            float tm = fmaxf(fmaxf(S[qt][0], S[qt][1]), S[qt][2]);
+#pragma unroll
+            for (int v = 3; v < 15; v += 2)
+                tm = fmaxf(fmaxf(tm, S[qt][v]), S[qt][v + 1]);
+            tm = fmaxf(tm, S[qt][15]);
+            tmax[qt] = halves_max(tm); // the row's maximum score in this tile
+            const bool first = (st.m[qt] == -__builtin_inff());
+            const float rel = first ? tmax[qt] : tmax[qt] - st.m[qt];
+            grow_any |= first ? (tmax[qt] > -__builtin_inff()) : (rel > kRescaleSlack);
+        }
+        if (__builtin_expect(__any(grow_any), 0)) { // rare after the first tile
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                // every row moves its max up to the tile max (if higher)
+                const bool first = (st.m[qt] == -__builtin_inff());
+                if (first) {
+                    if (tmax[qt] > -__builtin_inff())
+                        st.m[qt] = tmax[qt];
+                } else if (tmax[qt] > st.m[qt]) {
+                    const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - tmax[qt]);
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+                        acc[dt][qt] *= alpha;
+                    st.l[qt] *= alpha;
+                    st.z[qt] *= alpha;
+                    st.m[qt] = tmax[qt];
+                }
+            }
+        }
+
+        // 2. S_{i+1} = K_{i+1} Q^T ...
+        qk_tile<PRESET, NQT>(kn, QB, Sn);
+
+        // ... while S_i becomes P_i = exp2(S_i - m) (fp16), the sums
+        // l += sum P_i and z += sum P_i * zero, and the next P operand
+        // P_i * vscale
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            const float msub = (st.m[qt] == -__builtin_inff()) ? 0.0f : st.m[qt];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int v = 8 * s + 2 * j;
+                    const float p0 = __builtin_amdgcn_exp2f(S[qt][v] - msub);
+                    const float p1 = __builtin_amdgcn_exp2f(S[qt][v + 1] - msub);
+                    const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
+                    uint32_t vs = vr.vs[s][j], vz = vr.vz[s][j];
+                    if constexpr (MASKED) {
+                        const int t = tok0 + 16 * s + 8 * h + 2 * j;
+                        const uint32_t keep = ((t < erow[qt]) ? 0x0000FFFFu : 0u) | ((t + 1 < erow[qt]) ? 0xFFFF0000u : 0u);
+                        vs &= keep;
+                        vz &= keep;
+                    }
+                    st.l[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, st.l[qt], false);
+                    st.z[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vz), st.z[qt], false);
+                    Pp[qt][s].u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vs));
+                }
+        }
+        Vp[0] = vr.v[0];
+        Vp[1] = vr.v[1];
+        // P_i waits in AGPRs for the next step's P V MFMAs (which read their
+        // B operand from there), and its arithmetic stays next to the S_{i+1}
+        // products instead of sinking into the next step past the refill
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
-            S[qt] = Sn[qt];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                asm volatile("" : "+a"(Pp[qt][s].h));
+
+        // 3. refill: tiles up to i + DEPTH may use the slots read so far
+        if (issued < ntile) {
+            wait_lgkm0(); // this step's LDS reads are complete
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                if (issued < ntile && issued <= i + DEPTH) {
+                    issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + (issued % DEPTH) * kSlotBytes, voff,
+                                       voff_last, lane);
+                    ++issued;
+                }
+        }
     };
-    for (int i = 0; i < nfast; ++i)
-        step(i, std::false_type{});
-    for (int i = nfast; i < ntile; ++i)
-        step(i, std::true_type{});
+    int i = 0;
+    for (; i + 2 <= nfast; i += 2) {
+        step(i, SA, SB, std::false_type{});
+        step(i + 1, SB, SA, std::false_type{});
+    }
+    if (i < nfast) {
+        step(i, SA, SB, std::false_type{});
+        ++i;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+            SA[qt] = SB[qt];
+    }
+    for (; i < ntile; ++i) {
+        step(i, SA, SB, std::true_type{});
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+            SA[qt] = SB[qt];
+    }
+    // P V of the last tile
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const half8_t A = value_operand(Vp, dt, s);
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+                acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pp[qt][s].h, acc[dt][qt], 0, 0, 0);
+        }
     float mrow[NQT], lsum[NQT], zsum[NQT];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
         mrow[qt] = st.m[qt];
-        lsum[qt] = st.l[qt];
-        zsum[qt] = st.z[qt];
+        // softmax sums of the two lane halves (same rows, different tokens)
+        lsum[qt] = halves_sum(st.l[qt]);
+        zsum[qt] = halves_sum(st.z[qt]);
     }
 
     // ---------------------------------------------------------------- merge
-    // softmax sums of the two lane halves (same rows, different tokens)
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        lsum[qt] += __shfl_xor(lsum[qt], 32, 64);
-        zsum[qt] += __shfl_xor(zsum[qt], 32, 64);
-    }
-    __syncthreads(); // every wavefront is done with the ring and the query tile
+    __syncthreads(); // every wavefront is done with the ring and the query rows
     float *macc = reinterpret_cast<float *>(lds);               // [4][RP][kAccStride]
     float *mstat = macc + kWaves * RP * kAccStride;             // [4][RP] m, l, z, alpha
     float *rstat = mstat + kWaves * RP * 4;                     // [RP] L, Z, M
@@ -612,9 +789,9 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
         for (int aa = 0; aa < 4; ++aa)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int i = 8 * aa + 4 * h + j; // d-quad of C registers 4aa + j
+                const int ii = 8 * aa + 4 * h + j; // d-quad of C registers 4aa + j
                 const int v = 4 * aa + j;
-                *reinterpret_cast<float4 *>(dst + 4 * i) =
+                *reinterpret_cast<float4 *>(dst + 4 * ii) =
                     make_float4(acc[0][qt][v], acc[1][qt][v], acc[2][qt][v], acc[3][qt][v]);
             }
     }
@@ -749,13 +926,6 @@ hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s
         else
             hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 2>), grid, block, 0, s, a);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s)
-{
-    const dim3 grid((unsigned)(a.B * a.Hk * a.rows_pad / 4)), block(256);
-    hipLaunchKernelGGL(qprep_kernel, grid, block, 0, s, a);
     return hipGetLastError();
 }
 
