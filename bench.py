@@ -45,11 +45,64 @@ def parse():
                     help="back-to-back verify calls for the per-launch kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-reference", type=float, default=0.0, metavar="MB",
+                    help="instead of the benchmark, run 20 plain device-to-device copies of MB "
+                         "megabytes (the calibration kernel for the HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest():
+    """sha256 of the verify kernel source: counter readings taken on another
+    version of the kernel are not reported."""
+    import hashlib
+    path = os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", "verify.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per verify call from the committed counter summary of this
+    workload (profiles/traffic_<workload>.md), or None when there is none or
+    it was taken on a different version of the kernel source."""
+    path = os.path.join(TRAFFIC_DIR, "traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_verify_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_reference(mb):
+    """Plain device-to-device copies of a known size: what FETCH_SIZE and
+    WRITE_SIZE read for them calibrates the counters."""
+    import torch
+    n = int(mb * 1e6)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": n, "copies": 20}))
 
 
 def main():
     args = parse()
+    if args.copy_reference > 0:
+        copy_reference(args.copy_reference)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the verify path needs no "
               "communication; see DESIGN.md for how it would shard). Use --gpus 1.",
@@ -200,7 +253,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.workload),
             "kernel": "tqkv_verify (verify_kernel + combine_kernel when splits > 1)",
             "bytes_per_launch": kv_bytes + qo_bytes,
         },

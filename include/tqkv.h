@@ -115,10 +115,9 @@ int tqkv_store(const tqkv_cache *cache, const void *K, const void *V, const int3
  * on this cache and shape; 0 for invalid arguments. */
 int tqkv_verify_num_splits(const tqkv_cache *cache, int n_spec, int Hq, int num_splits);
 
-/* Device workspace tqkv_verify needs, returned through *bytes: the prepared
- * query operands of every (b, hk) unit (scaled, rotated for k3v4_nc, fp16)
- * and, when more than one key range is used, the partial softmax states.
- * Returns TQKV_OK or a negative tqkv_status. */
+/* Device workspace tqkv_verify needs, returned through *bytes: when more
+ * than one key range is used, the partial softmax states of every range
+ * (0 bytes otherwise).  Returns TQKV_OK or a negative tqkv_status. */
 int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int num_splits,
                                 size_t *bytes);
 
@@ -132,8 +131,9 @@ int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int
  *   num_splits  key-range partitions per (b, hk), 0 = auto (at most 256 are used)
  *   sm_scale  softmax scale, 0 = 1/sqrt(128)
  *   out       device, fp32 [n_spec, B, Hq, 128], 16-byte aligned
- *   workspace device, 256-byte aligned, >= tqkv_verify_workspace_bytes(...);
- *             its contents on entry do not matter and are overwritten
+ *   workspace device, 256-byte aligned, >= tqkv_verify_workspace_bytes(...)
+ *             (may be NULL when that is 0); its contents on entry do not
+ *             matter and are overwritten
  * Query head hq reads KV head hq / (Hq / Hk).  k3v4_nc queries are rotated by
  * the same normalised WHT as the keys.  Preconditions (device values):
  * n_spec <= seq_lens[b] <= max_seq and every token below seq_lens[b] was

@@ -52,14 +52,18 @@ int nblocks(int max_seq) { return (max_seq + kBlockTokens - 1) / kBlockTokens; }
 
 // Key-range partitions per (b, hk): one work-group of 4 wavefronts per
 // compute unit overall, at least one 32-token tile per wavefront.
-int plan_splits(const tqkv_cache *c, int num_splits, int cus)
+int plan_splits(const tqkv_cache *c, int num_splits, int cus, int rows)
 {
     const int units = c->B * c->Hk;
     const int tiles = (c->max_seq + 31) / 32;
     const int max_useful = (tiles + 3) / 4;
     int s = num_splits;
     if (s <= 0)
-        s = (cus + units - 1) / units;
+#ifdef TQKV_NQT1_WGS_PER_CU
+        s = (cus * (rows <= 32 ? TQKV_NQT1_WGS_PER_CU : 1) + units - 1) / units;
+#else
+        s = (cus + units - 1) / units + 0 * rows;
+#endif
     if (s > max_useful)
         s = max_useful;
     if (s > 256) // the combine kernel stages at most 256 ranges per row
@@ -155,7 +159,7 @@ int tqkv_verify_num_splits(const tqkv_cache *cache, int n_spec, int Hq, int num_
     int cus = current_device_cus();
     if (cus < 0)
         return 0;
-    return plan_splits(cache, num_splits, cus);
+    return plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec);
 }
 
 int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int num_splits,
@@ -172,7 +176,7 @@ int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int
     int cus = current_device_cus();
     if (cus < 0)
         return cus;
-    *bytes = workspace_for(cache, n_spec, Hq, plan_splits(cache, num_splits, cus));
+    *bytes = workspace_for(cache, n_spec, Hq, plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec));
     return TQKV_OK;
 }
 
@@ -196,7 +200,7 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
     int cus = current_device_cus();
     if (cus < 0)
         return cus;
-    const int splits = plan_splits(cache, num_splits, cus);
+    const int splits = plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec);
     const size_t need = workspace_for(cache, n_spec, Hq, splits);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)

@@ -74,13 +74,19 @@ __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // tile i has been read into registers, so kRing - 1 tiles stay in flight.
 // ---------------------------------------------------------------------------
 template <int PRESET> struct Ring;
+#ifndef TQKV_K3_DEPTH
+#define TQKV_K3_DEPTH 8
+#endif
+#ifndef TQKV_K8_DEPTH
+#define TQKV_K8_DEPTH 4
+#endif
 template <> struct Ring<kPresetK3V4> {
     static constexpr int kLoads = 4; // ceil(2 * 1920 / 1024)
-    static constexpr int kDepth = 8;
+    static constexpr int kDepth = TQKV_K3_DEPTH;
 };
 template <> struct Ring<kPresetK8V4> {
     static constexpr int kLoads = 7; // ceil(2 * 3168 / 1024)
-    static constexpr int kDepth = 4;
+    static constexpr int kDepth = TQKV_K8_DEPTH;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -397,8 +403,11 @@ __device__ inline half8_t hadamard_operand(int o, int ks, int h)
     return r.h;
 }
 
+#ifndef TQKV_NQT1_WGS_PER_CU
+#define TQKV_NQT1_WGS_PER_CU 1
+#endif
 template <int PRESET, int NQT>
-__global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
+__global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void verify_kernel(VerifyArgs a)
 {
     constexpr int RP = 32 * NQT; // padded rows
     constexpr int LPT = Ring<PRESET>::kLoads, DEPTH = Ring<PRESET>::kDepth;
@@ -595,7 +604,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
     //      tile maximum of S_i (VALU), then rescales if a row maximum grew;
     //   2. computes S_{i+1} = K_{i+1} Q^T (MFMA) while it turns S_i into the
     //      probabilities P_i and their sums (VALU);
-    //   3. refills the ring.
+    //   3. refills the ring, one tile after each of the two parts.
     // Two score buffers alternate between the steps.
     floatx16 SA[NQT], SB[NQT];
     H8 Pp[NQT][2]; // P operand of the previous tile (zero before the first)
@@ -616,6 +625,16 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
     // tiles [0, nfast) need no masking; the rest (the sequence's last tile
     // and the causal window) run in a separate loop
     const int nfast = max(0, min(ntile, (emin - kt0 * kTile) / kTile));
+    // one more ring tile, if one is pending and its slot has been read
+    // (tiles up to i + DEPTH may reuse the slots of tiles <= i)
+    auto refill = [&](int i) {
+        if (issued < ntile && issued <= i + DEPTH) {
+            wait_lgkm0(); // the slot's LDS reads are complete
+            issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + (issued % DEPTH) * kSlotBytes, voff,
+                               voff_last, lane);
+            ++issued;
+        }
+    };
     auto step = [&](int i, floatx16(&S)[NQT], floatx16(&Sn)[NQT], auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int kt = kt0 + i;
@@ -662,6 +681,9 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
             const float rel = first ? tmax[qt] : tmax[qt] - st.m[qt];
             grow_any |= first ? (tmax[qt] > -__builtin_inff()) : (rel > kRescaleSlack);
         }
+        // the loads of one ring tile go out between the two MFMA groups, so
+        // that a full memory pipeline delays this wavefront only briefly
+        refill(i);
         if (__builtin_expect(__any(grow_any), 0)) { // rare after the first tile
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -722,17 +744,8 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(VerifyArgs a)
             for (int s = 0; s < 2; ++s)
                 asm volatile("" : "+a"(Pp[qt][s].h));
 
-        // 3. refill: tiles up to i + DEPTH may use the slots read so far
-        if (issued < ntile) {
-            wait_lgkm0(); // this step's LDS reads are complete
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-                if (issued < ntile && issued <= i + DEPTH) {
-                    issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + (issued % DEPTH) * kSlotBytes, voff,
-                                       voff_last, lane);
-                    ++issued;
-                }
-        }
+        // 3. and the loads of another (while the ring is still filling)
+        refill(i);
     };
     int i = 0;
     for (; i + 2 <= nfast; i += 2) {
