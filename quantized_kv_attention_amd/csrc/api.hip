@@ -50,24 +50,24 @@ int check_cache(const tqkv_cache *c)
 
 int nblocks(int max_seq) { return (max_seq + kBlockTokens - 1) / kBlockTokens; }
 
-// Key-range partitions per (b, hk): one work-group of 4 wavefronts per
+// Query rows per work-group: the rows of one KV head are cut into tiles of
+// 32 (one MFMA operand height), one work-group each.
+int row_tiles(int rows) { return (rows + 31) / 32; }
+
+// Key-range partitions per (b, hk): two work-groups of 4 wavefronts per
 // compute unit overall, at least one 32-token tile per wavefront.
 int plan_splits(const tqkv_cache *c, int num_splits, int cus, int rows)
 {
-    const int units = c->B * c->Hk;
+    const int units = c->B * c->Hk * row_tiles(rows);
     const int tiles = (c->max_seq + 31) / 32;
     const int max_useful = (tiles + 3) / 4;
     int s = num_splits;
     if (s <= 0)
-#ifdef TQKV_NQT1_WGS_PER_CU
-        s = (cus * (rows <= 32 ? TQKV_NQT1_WGS_PER_CU : 1) + units - 1) / units;
-#else
-        s = (cus + units - 1) / units + 0 * rows;
-#endif
+        s = (2 * cus + units - 1) / units;
     if (s > max_useful)
         s = max_useful;
-    if (s > 256) // the combine kernel stages at most 256 ranges per row
-        s = 256;
+    if (s > 1024)
+        s = 1024;
     if (s < 1)
         s = 1;
     return s;
@@ -87,14 +87,15 @@ int check_verify_shape(const tqkv_cache *c, int n_spec, int Hq)
     return TQKV_OK;
 }
 
-// Workspace: with more than one key range, the normalised partial outputs
-// and their (max, sum); nothing otherwise.
+// Workspace: with more than one key range, the partial softmax states of
+// every key range (32 rows per row tile); nothing otherwise.
 size_t workspace_for(const tqkv_cache *c, int n_spec, int Hq, int splits)
 {
     if (splits <= 1)
         return 0;
-    const size_t rows = (size_t)c->B * c->Hk * splits * (size_t)((Hq / c->Hk) * n_spec);
-    return rows * TQKV_HEAD_DIM * sizeof(float) + rows * 2 * sizeof(float);
+    const size_t groups = (size_t)c->B * c->Hk * row_tiles((Hq / c->Hk) * n_spec);
+    const size_t slots = groups * splits * 32;
+    return slots * TQKV_HEAD_DIM * sizeof(float) + slots * 2 * sizeof(float);
 }
 
 } // namespace
@@ -216,10 +217,10 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
     a.Q = Q;
     a.seq_lens = seq_lens;
     a.out = out;
-    const size_t units_rows = (size_t)cache->B * cache->Hk * splits * R;
-    float *part = static_cast<float *>(workspace);
-    a.part_o = splits > 1 ? part : nullptr;
-    a.part_ml = splits > 1 ? reinterpret_cast<float2 *>(part + units_rows * TQKV_HEAD_DIM) : nullptr;
+    const size_t groups = (size_t)cache->B * cache->Hk * row_tiles(R);
+    float *part = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    a.part_o = part;
+    a.part_ml = splits > 1 ? reinterpret_cast<float2 *>(part + groups * splits * 32 * TQKV_HEAD_DIM) : nullptr;
     a.qscale = scale * 1.4426950408889634f;
     a.q_f16 = (q_dtype == TQKV_Q_F16);
     a.Hk = cache->Hk;
@@ -232,24 +233,10 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
     a.R = R;
     a.causal = causal;
     a.nsplit = splits;
+    a.nrt = row_tiles(R);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_verify(cache->preset, R <= 32 ? 1 : 2, a, s) != hipSuccess)
+    if (launch_verify(cache->preset, 1, a, s) != hipSuccess)
         return TQKV_ERR_LAUNCH;
-    if (splits > 1) {
-        CombineArgs c;
-        c.part_o = a.part_o;
-        c.part_ml = a.part_ml;
-        c.out = out;
-        c.B = cache->B;
-        c.Hk = cache->Hk;
-        c.N = n_spec;
-        c.Hq = Hq;
-        c.G = G;
-        c.R = R;
-        c.nsplit = splits;
-        if (launch_combine(c, s) != hipSuccess)
-            return TQKV_ERR_LAUNCH;
-    }
     return TQKV_OK;
 }
 

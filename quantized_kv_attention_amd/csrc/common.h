@@ -63,25 +63,19 @@ struct VerifyArgs {
     const uint8_t *base;
     const void *Q;   // [N, B, Hq, 128], fp32 or fp16 (q_f16)
     const int32_t *seq_lens;
-    float *out;      // final output (nsplit == 1)
-    float *part_o;   // [units * nsplit * R][128] normalised partial outputs
-    float2 *part_ml; // [units * nsplit * R] (running max in log2 units, softmax sum)
-    float qscale;    // softmax scale * log2(e)
+    float *out;      // [N, B, Hq, 128]
+    // partial states of the key ranges (nsplit > 1), per (unit, row tile) g:
+    float *part_o;   // [g][nsplit][32 rows][128] normalised partial outputs
+    float2 *part_ml; // [g][nsplit][32 rows] (running max in log2 units, softmax sum)
+    float qscale;       // softmax scale * log2(e)
     int q_f16;
     int Hk, max_seq, nblk;
     int B, N, Hq, G, R, causal, nsplit;
-};
-
-struct CombineArgs {
-    const float *part_o;
-    const float2 *part_ml;
-    float *out;
-    int B, Hk, N, Hq, G, R, nsplit;
+    int nrt; // row tiles per (b, hk): one work-group each
 };
 
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
 hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s);
-hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 } // namespace tqkv

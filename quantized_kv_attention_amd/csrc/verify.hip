@@ -49,7 +49,6 @@ constexpr int kTile = 32;        // tokens per inner-loop step
 constexpr int kWaves = 4;        // wavefronts per work-group
 constexpr int kQStride = 136;    // halfs per fp16 query row in LDS (128 + 8: no bank collisions
                                  // between the 32 rows an MFMA operand read touches)
-constexpr int kAccStride = 132;  // floats per row of the LDS merge buffer
 constexpr int kInitTiles = 2;    // ring tiles issued before the query preparation
 
 union H8 {
@@ -73,20 +72,16 @@ __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // the query prologue, and slot i is refilled with tile i + kRing as soon as
 // tile i has been read into registers, so kRing - 1 tiles stay in flight.
 // ---------------------------------------------------------------------------
+// The depth is chosen so that a 32-row work-group fits in 80 KiB of LDS
+// (two work-groups per compute unit).
 template <int PRESET> struct Ring;
-#ifndef TQKV_K3_DEPTH
-#define TQKV_K3_DEPTH 8
-#endif
-#ifndef TQKV_K8_DEPTH
-#define TQKV_K8_DEPTH 4
-#endif
 template <> struct Ring<kPresetK3V4> {
     static constexpr int kLoads = 4; // ceil(2 * 1920 / 1024)
-    static constexpr int kDepth = TQKV_K3_DEPTH;
+    static constexpr int kDepth = 4;
 };
 template <> struct Ring<kPresetK8V4> {
     static constexpr int kLoads = 7; // ceil(2 * 3168 / 1024)
-    static constexpr int kDepth = TQKV_K8_DEPTH;
+    static constexpr int kDepth = 2;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -403,11 +398,8 @@ __device__ inline half8_t hadamard_operand(int o, int ks, int h)
     return r.h;
 }
 
-#ifndef TQKV_NQT1_WGS_PER_CU
-#define TQKV_NQT1_WGS_PER_CU 1
-#endif
 template <int PRESET, int NQT>
-__global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void verify_kernel(VerifyArgs a)
+__global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArgs a)
 {
     constexpr int RP = 32 * NQT; // padded rows
     constexpr int LPT = Ring<PRESET>::kLoads, DEPTH = Ring<PRESET>::kDepth;
@@ -417,7 +409,10 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
     constexpr int kQRegion = RP * kD * 4;
     static_assert(RP * kQStride * 2 <= kQRegion, "query region");
     constexpr int kRingBytes = kWaves * DEPTH * kSlotBytes;
-    constexpr int kMergeBytes = (kWaves * RP * kAccStride + kWaves * RP * 4 + RP * 3) * 4;
+    // merge region: every wavefront's accumulator slots + per-row states
+    constexpr int kCombos = 4 * NQT; // (row tile, C-register quad) pairs
+    constexpr int kXBytes = kWaves * kCombos * 4 * 64 * 16;
+    constexpr int kMergeBytes = kXBytes + kWaves * RP * 16;
     constexpr int kLdsBytes = (kQRegion + kRingBytes) > kMergeBytes ? (kQRegion + kRingBytes) : kMergeBytes;
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -427,10 +422,24 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
     // range, the ring slot, the wait counts) stays in SGPRs and uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, col = lane & 31;
-    const int unit = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
+    // work item of this work-group: (unit, key range, row tile).  Work-groups
+    // are dealt to the 8 XCDs round-robin by index; consecutive items (the
+    // row tiles and neighbouring key ranges of one unit) go to one XCD, so
+    // they share its L2 (tiles read twice, partial results)
+    int item = blockIdx.x;
+    if ((gridDim.x & 7) == 0)
+        item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int rt = item % a.nrt, us = item / a.nrt;
+    const int unit = us / a.nsplit, split = us % a.nsplit;
+    const int row0 = RP * rt; // first query row of this work-group
     const int b = unit / a.Hk, hk = unit % a.Hk;
     const int Lr = a.seq_lens[b];
     const int L = Lr < 0 ? 0 : (Lr > a.max_seq ? a.max_seq : Lr);
+    // row r of the unit is query head hk * G + r % G of speculative token
+    // r / G; the quotient comes from a float reciprocal (exact: r < 64 and
+    // (r + 0.5) / G stays at least 0.5 / G away from an integer)
+    const float rcpG = __builtin_amdgcn_rcpf((float)a.G);
+    auto row_token = [&](int r) { return (int)(((float)r + 0.5f) * rcpG); };
 
     // this wavefront's tiles [kt0, kt1): the unit's tiles are cut into
     // nsplit work-group ranges, each range into 4 wavefront runs
@@ -450,8 +459,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
 
     // ------------------------------------------------------------ prologue
     // 1. The unit's raw query rows -> LDS, 1 KiB per load (2 fp32 or 4 fp16
-    //    rows).  Row r = n * G + g is query head hk * G + g of speculative
-    //    token n; padding rows re-read row 0 and are zeroed below.  Every
+    //    rows).  Padding rows re-read row 0 and are zeroed below.  Every
     //    wavefront queues these loads before any wavefront queues ring loads,
     //    so the query does not wait behind the key stream.
     {
@@ -460,9 +468,9 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
         const int rpi = 64 >> rshift;       // rows per load
         const int rsub = lane >> rshift, cb = 16 * (lane & ((1 << rshift) - 1));
         for (int J = wave; J < RP / rpi; J += kWaves) {
-            const int r = J * rpi + rsub;
+            const int r = row0 + J * rpi + rsub;
             const int rs = r < a.R ? r : 0;
-            const int n = rs / a.G, g = rs % a.G;
+            const int n = row_token(rs), g = rs - n * a.G;
             const uint8_t *src = static_cast<const uint8_t *>(a.Q) +
                                  ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD * esz + cb;
             dma16(src, lds0 + 1024 * J);
@@ -479,10 +487,46 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
     int issued = 0; // tiles of this wavefront issued so far (wave-uniform)
     for (; issued < min(kInitTiles, ntile); ++issued)
         issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + issued * kSlotBytes, voff, voff_last, lane);
-    wait_ring<LPT>(issued); // this wavefront's query loads have landed
-    lds_barrier();        // ... and every other wavefront's
 
-    // 3. scale (softmax scale * log2 e: the softmax runs in base 2) and round
+    // 3. state set-up while the loads are in flight
+    int erow[NQT]; // effective end of this lane's query rows (causal window)
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const int rr = row0 + 32 * qt + col;
+        const int n = row_token(rr);
+        erow[qt] = (rr < a.R) ? (a.causal ? min(L - a.N + n + 1, L) : L) : 0;
+    }
+    // every row sees every token below emin: tiles ending there need no mask
+    const int emin = a.causal ? (L - a.N + 1) : L;
+    floatx16 acc[4][NQT];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            acc[dt][qt] = floatx16{0};
+            asm volatile("" : "+v"(acc[dt][qt])); // zeroed here, under the load latency
+        }
+    SoftState<NQT> st;
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        st.m[qt] = -__builtin_inff();
+        st.l[qt] = 0.0f;
+        st.z[qt] = 0.0f;
+    }
+    H8 Pp[NQT][2]; // P_{i-1} * vscale: the B operands of the pending P V
+    u32x4 Vp[2];   // value nibbles of tile i-1 (A operands of the pending P V)
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            Pp[qt][s].h = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    Vp[0] = u32x4{0, 0, 0, 0};
+    Vp[1] = u32x4{0, 0, 0, 0};
+
+    wait_ring<LPT>(issued); // this wavefront's query loads have landed
+    lds_barrier();          // ... and every other wavefront's
+
+    // 4. scale (softmax scale * log2 e: the softmax runs in base 2) and round
     //    to binary16; thread t converts CPT coordinates of row t / TPR
     constexpr int CPT = 16 * NQT, TPR = kD / CPT;
     {
@@ -509,7 +553,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
                 qh[c / 2 + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale)});
             }
         }
-        if (rr >= a.R) {
+        if (row0 + rr >= a.R) {
 #pragma unroll
             for (int j = 0; j < CPT / 2; ++j)
                 qh[j] = 0u;
@@ -522,7 +566,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
         lds_barrier();
     }
 
-    // 4. k3v4_nc: rotate by the normalised WHT, q' = H q / sqrt(128), as the
+    // 5. k3v4_nc: rotate by the normalised WHT, q' = H q / sqrt(128), as the
     //    MFMA product Q'^T = H Q^T; wavefront w computes output coordinates
     //    32w..32w+31 of every row and writes them back in place
     if constexpr (PRESET == kPresetK3V4) {
@@ -559,7 +603,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
         lds_barrier();
     }
 
-    // 5. the QK^T B operands, held in registers for the whole key loop
+    // 6. the QK^T B operands, held in registers for the whole key loop
     half8_t QB[NQT][8];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
@@ -574,57 +618,20 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
         for (int ks = 0; ks < 8; ++ks)
             asm volatile("" : "+a"(QB[qt][ks]));
 
-    // Effective end of this lane's query rows (causal window of the pages).
-    int erow[NQT];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        const int rr = 32 * qt + col;
-        const int n = rr / a.G;
-        erow[qt] = (rr < a.R) ? (a.causal ? min(L - a.N + n + 1, L) : L) : 0;
-    }
-    const int emin = a.causal ? (L - a.N + 1) : L;
-
-    floatx16 acc[4][NQT];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
-            acc[dt][qt] = floatx16{0};
-    SoftState<NQT> st;
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        st.m[qt] = -__builtin_inff();
-        st.l[qt] = 0.0f;
-        st.z[qt] = 0.0f;
-    }
-
-    // Software pipeline over the wavefront's tiles.  Step i takes the scores
-    // S_i (computed one step earlier) and
-    //   1. adds P_{i-1} V_{i-1} to the accumulators (MFMA) while it finds the
-    //      tile maximum of S_i (VALU), then rescales if a row maximum grew;
-    //   2. computes S_{i+1} = K_{i+1} Q^T (MFMA) while it turns S_i into the
-    //      probabilities P_i and their sums (VALU);
-    //   3. refills the ring, one tile after each of the two parts.
-    // Two score buffers alternate between the steps.
-    floatx16 SA[NQT], SB[NQT];
-    H8 Pp[NQT][2]; // P operand of the previous tile (zero before the first)
-    u32x4 Vp[2];   // value nibbles of the previous tile
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            Pp[qt][s].h = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    Vp[0] = u32x4{0, 0, 0, 0};
-    Vp[1] = u32x4{0, 0, 0, 0};
-    if (ntile > 0) {
-        wait_ring<LPT>(issued - 1);
-        KeyRegs<PRESET> k0;
-        read_keys<PRESET>(k0, ring, lane);
-        qk_tile<PRESET, NQT>(k0, QB, SA);
-    }
-    // tiles [0, nfast) need no masking; the rest (the sequence's last tile
-    // and the causal window) run in a separate loop
-    const int nfast = max(0, min(ntile, (emin - kt0 * kTile) / kTile));
+    // ------------------------------------------------------------ key loop
+    // One step per tile i.  The scores S_i were computed by the step before
+    // (the prologue for i = 0).  Step i
+    //   1. finds the tile maximum of S_i per row and, when a row maximum grew
+    //      (rare after the first tile), rescales the accumulators and the
+    //      pending probabilities P_{i-1};
+    //   2. adds P_{i-1} V_{i-1} to the accumulators (MFMA) while it turns S_i
+    //      into P_i and the sums l, z (VALU), the two interleaved;
+    //   3. computes S_{i+1} = K_{i+1} Q^T (MFMA, the key dequantisation
+    //      interleaved).
+    // The value operands of P V are built from the nibbles right before
+    // their MFMAs.  One score buffer suffices: S_i is consumed before
+    // S_{i+1} is written.
+    floatx16 S[NQT];
     // one more ring tile, if one is pending and its slot has been read
     // (tiles up to i + DEPTH may reuse the slots of tiles <= i)
     auto refill = [&](int i) {
@@ -635,12 +642,16 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
             ++issued;
         }
     };
-    auto step = [&](int i, floatx16(&S)[NQT], floatx16(&Sn)[NQT], auto masked_tag) {
+    if (ntile > 0) {
+        wait_ring<LPT>(issued - 1);
+        KeyRegs<PRESET> k0;
+        read_keys<PRESET>(k0, ring, lane);
+        qk_tile<PRESET, NQT>(k0, QB, S);
+    }
+    auto step = [&](int i, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int kt = kt0 + i;
-        const int tok0 = kt * kTile;
-        // this tile's value fields and the next tile's keys (the last step
-        // re-reads its own keys; that product is never used)
+        const int tok0 = (kt0 + i) * kTile;
+        // the next tile's keys (the last step re-reads its own; the product is unused)
         int inext = i;
         if (i + 1 < ntile) {
             wait_ring<LPT>(issued - i - 2);
@@ -648,55 +659,51 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
         }
         ValRegs vr;
         read_values<PRESET>(vr, ring + (i % DEPTH) * kSlotBytes, lane);
-        KeyRegs<PRESET> kn;
-        read_keys<PRESET>(kn, ring + (inext % DEPTH) * kSlotBytes, lane);
 
-        // 1. O^T += V_{i-1}^T P_{i-1}^T; tile maximum of S_i; lazy rescale
+        // 1. tile maximum per row; lazy rescale
+        // C register v of the lane holds token tok0 + 8h + 16 (v / 8) + v % 8;
+        // lim[qt] = how many of the tile's tokens past tok0 + 8h the row sees
+        int lim[NQT];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int qt = 0; qt < NQT; ++qt)
+            lim[qt] = erow[qt] - tok0 - 8 * h;
+        if constexpr (MASKED) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const half8_t A = value_operand(Vp, dt, s);
+            for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-                for (int qt = 0; qt < NQT; ++qt)
-                    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pp[qt][s].h, acc[dt][qt], 0, 0, 0);
-            }
+                for (int v = 0; v < 16; ++v)
+                    if (16 * (v >> 3) + (v & 7) >= lim[qt])
+                        S[qt][v] = -__builtin_inff();
+        }
         float tmax[NQT];
         bool grow_any = false;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
-            if constexpr (MASKED) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    if (tok0 + 16 * (v >> 3) + 8 * h + (v & 7) >= erow[qt])
-                        S[qt][v] = -__builtin_inff();
-            }
             float tm = fmaxf(fmaxf(S[qt][0], S[qt][1]), S[qt][2]);
 #pragma unroll
             for (int v = 3; v < 15; v += 2)
                 tm = fmaxf(fmaxf(tm, S[qt][v]), S[qt][v + 1]);
             tm = fmaxf(tm, S[qt][15]);
             tmax[qt] = halves_max(tm); // the row's maximum score in this tile
-            const bool first = (st.m[qt] == -__builtin_inff());
-            const float rel = first ? tmax[qt] : tmax[qt] - st.m[qt];
-            grow_any |= first ? (tmax[qt] > -__builtin_inff()) : (rel > kRescaleSlack);
+            grow_any |= (st.m[qt] == -__builtin_inff()) ? (tmax[qt] > -__builtin_inff())
+                                                          : (tmax[qt] - st.m[qt] > kRescaleSlack);
         }
-        // the loads of one ring tile go out between the two MFMA groups, so
-        // that a full memory pipeline delays this wavefront only briefly
-        refill(i);
-        if (__builtin_expect(__any(grow_any), 0)) { // rare after the first tile
+        if (__builtin_expect(__any(grow_any), 0)) {
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
-                // every row moves its max up to the tile max (if higher)
-                const bool first = (st.m[qt] == -__builtin_inff());
-                if (first) {
-                    if (tmax[qt] > -__builtin_inff())
-                        st.m[qt] = tmax[qt];
-                } else if (tmax[qt] > st.m[qt]) {
-                    const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - tmax[qt]);
+                // every row moves its max up to the tile max (if higher); the
+                // accumulators and P_{i-1} (both relative to the old max)
+                // shrink by alpha; a row that had no max yet holds zeros
+                if (tmax[qt] > st.m[qt]) {
+                    const float alpha = (st.m[qt] == -__builtin_inff()) ? 0.0f
+                                                                         : __builtin_amdgcn_exp2f(st.m[qt] - tmax[qt]);
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt)
                         acc[dt][qt] *= alpha;
+                    const _Float16 ah = (_Float16)alpha;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        Pp[qt][s].h *= ah;
                     st.l[qt] *= alpha;
                     st.z[qt] *= alpha;
                     st.m[qt] = tmax[qt];
@@ -704,179 +711,212 @@ __global__ __launch_bounds__(256, NQT == 1 ? TQKV_NQT1_WGS_PER_CU : 1) void veri
             }
         }
 
-        // 2. S_{i+1} = K_{i+1} Q^T ...
-        qk_tile<PRESET, NQT>(kn, QB, Sn);
-
-        // ... while S_i becomes P_i = exp2(S_i - m) (fp16), the sums
-        // l += sum P_i and z += sum P_i * zero, and the next P operand
-        // P_i * vscale
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            const float msub = (st.m[qt] == -__builtin_inff()) ? 0.0f : st.m[qt];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int v = 8 * s + 2 * j;
-                    const float p0 = __builtin_amdgcn_exp2f(S[qt][v] - msub);
-                    const float p1 = __builtin_amdgcn_exp2f(S[qt][v + 1] - msub);
-                    const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
-                    uint32_t vs = vr.vs[s][j], vz = vr.vz[s][j];
-                    if constexpr (MASKED) {
-                        const int t = tok0 + 16 * s + 8 * h + 2 * j;
-                        const uint32_t keep = ((t < erow[qt]) ? 0x0000FFFFu : 0u) | ((t + 1 < erow[qt]) ? 0xFFFF0000u : 0u);
-                        vs &= keep;
-                        vz &= keep;
-                    }
-                    st.l[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, st.l[qt], false);
-                    st.z[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vz), st.z[qt], false);
-                    Pp[qt][s].u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vs));
-                }
-        }
-        Vp[0] = vr.v[0];
-        Vp[1] = vr.v[1];
-        // P_i waits in AGPRs for the next step's P V MFMAs (which read their
-        // B operand from there), and its arithmetic stays next to the S_{i+1}
-        // products instead of sinking into the next step past the refill
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                asm volatile("" : "+a"(Pp[qt][s].h));
-
-        // 3. and the loads of another (while the ring is still filling)
-        refill(i);
-    };
-    int i = 0;
-    for (; i + 2 <= nfast; i += 2) {
-        step(i, SA, SB, std::false_type{});
-        step(i + 1, SB, SA, std::false_type{});
-    }
-    if (i < nfast) {
-        step(i, SA, SB, std::false_type{});
-        ++i;
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
-            SA[qt] = SB[qt];
-    }
-    for (; i < ntile; ++i) {
-        step(i, SA, SB, std::true_type{});
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
-            SA[qt] = SB[qt];
-    }
-    // P V of the last tile
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const half8_t A = value_operand(Vp, dt, s);
+        // 2. O^T += V_{i-1}^T P_{i-1}^T (MFMA, zero operands at i = 0) while
+        //    S_i becomes P_i = exp2(S_i - m) (fp16), l += sum P_i,
+        //    z += sum P_i * zero and the next B operand P_i * vscale (VALU).
+        //    The two are interleaved by hand: after each MFMA one share of
+        //    the softmax work (two scores of both lane halves), with the
+        //    compiler's scheduler fenced off so the pairing stays.
+        {
+            float msub[NQT];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt)
-                acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Pp[qt][s].h, acc[dt][qt], 0, 0, 0);
-        }
-    float mrow[NQT], lsum[NQT], zsum[NQT];
+                msub[qt] = (st.m[qt] == -__builtin_inff()) ? 0.0f : st.m[qt];
+            H8 Pn[NQT][2];
+            auto softmax_share = [&](int qt, int s, int j) {
+                const int v = 8 * s + 2 * j;
+                const float p0 = __builtin_amdgcn_exp2f(S[qt][v] - msub[qt]);
+                const float p1 = __builtin_amdgcn_exp2f(S[qt][v + 1] - msub[qt]);
+                const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
+                uint32_t vs = vr.vs[s][j], vz = vr.vz[s][j];
+                if constexpr (MASKED) {
+                    // fields of invisible tokens never enter (they may hold anything)
+                    const uint32_t keep = ((16 * s + 2 * j < lim[qt]) ? 0x0000FFFFu : 0u) |
+                                          ((16 * s + 2 * j + 1 < lim[qt]) ? 0xFFFF0000u : 0u);
+                    vs &= keep;
+                    vz &= keep;
+                }
+                st.l[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, st.l[qt], false);
+                st.z[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vz), st.z[qt], false);
+                Pn[qt][s].u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vs));
+            };
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        mrow[qt] = st.m[qt];
-        // softmax sums of the two lane halves (same rows, different tokens)
-        lsum[qt] = halves_sum(st.l[qt]);
-        zsum[qt] = halves_sum(st.z[qt]);
-    }
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(Vp, dt, s), Pp[qt][s].h,
+                                                                             acc[dt][qt], 0, 0, 0);
+                        softmax_share(qt, s, dt); // 16 NQT shares: (qt, s, j = dt)
+                        if constexpr (!MASKED)
+                            __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    Pp[qt][s] = Pn[qt][s];
+            // the new P and sums are complete here: their arithmetic must not
+            // sink past the ring refill into the next part
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    asm volatile("" : "+v"(Pp[qt][s].h));
+                asm volatile("" : "+v"(st.l[qt]), "+v"(st.z[qt]));
+            }
+        }
+        refill(i);
+
+        // 3. S_{i+1} = K_{i+1} Q^T (MFMA; the keys become operands on the way)
+        KeyRegs<PRESET> kn;
+        read_keys<PRESET>(kn, ring + (inext % DEPTH) * kSlotBytes, lane);
+        qk_tile<PRESET, NQT>(kn, QB, S);
+        Vp[0] = vr.v[0];
+        Vp[1] = vr.v[1];
+        refill(i);
+    };
+
+    // tiles [0, nfast) need no mask; the sequence's last tiles (the causal
+    // window and the partial tail) run through the masked variant
+    const int nfast = max(0, min(ntile, (emin - kt0 * kTile) / kTile));
+    int i = 0;
+    for (; i < nfast; ++i)
+        step(i, std::false_type{});
+    for (; i < ntile; ++i)
+        step(i, std::true_type{});
+    // P V of the last tile
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(Vp, dt, s), Pp[qt][s].h, acc[dt][qt], 0, 0, 0);
 
     // ---------------------------------------------------------------- merge
+    // The four wavefronts hold softmax states of the same 32 rows over
+    // different tokens.  Each stores its accumulators in LDS in register
+    // layout (lane-major float4s, no repacking) and its row states; wavefront
+    // w then reduces C-register quad aa = w of all four: lane (col, h) ends
+    // up with row lrow = col, coordinates d = 4 (8w + 4h + j) + dt
+    // (j, dt = 0..3), i.e. four float4s of the output row.
+    static_assert(NQT == 1, "one 32-row tile per work-group");
     __syncthreads(); // every wavefront is done with the ring and the query rows
-    float *macc = reinterpret_cast<float *>(lds);               // [4][RP][kAccStride]
-    float *mstat = macc + kWaves * RP * kAccStride;             // [4][RP] m, l, z, alpha
-    float *rstat = mstat + kWaves * RP * 4;                     // [RP] L, Z, M
+    float4 *xbuf = reinterpret_cast<float4 *>(lds);           // [w][aa][dt][lane]
+    float4 *sbuf = reinterpret_cast<float4 *>(lds + kXBytes); // [w][row]: m, l, z
+    {
+        // softmax sums of the two lane halves (same rows, different tokens)
+        const float ls = halves_sum(st.l[0]), zs = halves_sum(st.z[0]);
+        if (h == 0)
+            sbuf[wave * RP + col] = make_float4(st.m[0], ls, zs, 0.0f);
+    }
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        const int rr = 32 * qt + col;
-        if (h == 0) {
-            mstat[(wave * RP + rr) * 4 + 0] = mrow[qt];
-            mstat[(wave * RP + rr) * 4 + 1] = lsum[qt];
-            mstat[(wave * RP + rr) * 4 + 2] = zsum[qt];
+    for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            xbuf[((wave * 4 + aa) * 4 + dt) * 64 + lane] =
+                make_float4(acc[dt][0][4 * aa], acc[dt][0][4 * aa + 1], acc[dt][0][4 * aa + 2], acc[dt][0][4 * aa + 3]);
+    __syncthreads();
+    const int lrow = col, row = row0 + lrow;
+    float M = -__builtin_inff();
+    float4 ms[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        ms[w] = sbuf[w * RP + lrow];
+        M = fmaxf(M, ms[w].x);
+    }
+    float al[kWaves], Ls = 0.0f, Zs = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        al[w] = (ms[w].x == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms[w].x - M);
+        Ls = __builtin_fmaf(al[w], ms[w].y, Ls);
+        Zs = __builtin_fmaf(al[w], ms[w].z, Zs);
+    }
+    // normalised output O = (sum_w al_w acc_w * 2^24 (even d) or 2^20 (odd d)
+    // + Zs) / Ls: the value operand carried c * 2^-24 (even d) and 16c * 2^-24
+    // (odd d).  Ls == 0: the row saw no token here (weight 0 below, NaN if
+    // nothing else contributes); a NaN Ls propagates.
+    const float inv = (Ls != 0.0f) ? 1.0f / Ls : 0.0f;
+    float O[4][4]; // [j][dt]: coordinate 4 (8 wave + 4h + j) + dt
+    {
+        float ke[kWaves], ko[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            ke[w] = al[w] * (16777216.0f * inv);
+            ko[w] = al[w] * (1048576.0f * inv);
         }
-        float *dst = macc + (wave * RP + rr) * kAccStride;
+        const float zo = Zs * inv;
 #pragma unroll
-        for (int aa = 0; aa < 4; ++aa)
+        for (int dt = 0; dt < 4; ++dt) {
+            const float *kw = (dt & 1) ? ko : ke;
+            float o[4] = {zo, zo, zo, zo};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int ii = 8 * aa + 4 * h + j; // d-quad of C registers 4aa + j
-                const int v = 4 * aa + j;
-                *reinterpret_cast<float4 *>(dst + 4 * ii) =
-                    make_float4(acc[0][qt][v], acc[1][qt][v], acc[2][qt][v], acc[3][qt][v]);
+            for (int w = 0; w < kWaves; ++w) {
+                const float4 x = xbuf[((w * 4 + wave) * 4 + dt) * 64 + lane];
+                o[0] = __builtin_fmaf(kw[w], x.x, o[0]);
+                o[1] = __builtin_fmaf(kw[w], x.y, o[1]);
+                o[2] = __builtin_fmaf(kw[w], x.z, o[2]);
+                o[3] = __builtin_fmaf(kw[w], x.w, o[3]);
             }
-    }
-    __syncthreads();
-    if (threadIdx.x < RP) {
-        const int rr = threadIdx.x;
-        float M = -__builtin_inff();
-        for (int w = 0; w < kWaves; ++w)
-            M = fmaxf(M, mstat[(w * RP + rr) * 4 + 0]);
-        float Ls = 0.0f, Zs = 0.0f;
-        for (int w = 0; w < kWaves; ++w) {
-            const float mw = mstat[(w * RP + rr) * 4 + 0];
-            const float al = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            mstat[(w * RP + rr) * 4 + 3] = al;
-            Ls += al * mstat[(w * RP + rr) * 4 + 1];
-            Zs += al * mstat[(w * RP + rr) * 4 + 2];
-        }
-        rstat[rr * 3 + 0] = Ls;
-        rstat[rr * 3 + 1] = Zs;
-        rstat[rr * 3 + 2] = M;
-    }
-    __syncthreads();
-    const size_t pbase = ((size_t)unit * a.nsplit + split) * a.R;
-    for (int e4 = threadIdx.x; e4 < a.R * (kD / 4); e4 += 256) {
-        const int rr = e4 >> 5, d = (e4 & 31) * 4;
-        float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float al = mstat[(w * RP + rr) * 4 + 3];
-            const float4 x = *reinterpret_cast<const float4 *>(macc + (w * RP + rr) * kAccStride + d);
-            s4.x += al * x.x;
-            s4.y += al * x.y;
-            s4.z += al * x.z;
-            s4.w += al * x.w;
-        }
-        const float Ls = rstat[rr * 3 + 0], Zs = rstat[rr * 3 + 1];
-        // the value operand carried c * 2^-24 (even d) and 16c * 2^-24 (odd d)
-        float4 o = make_float4(s4.x * 16777216.0f + Zs, s4.y * 1048576.0f + Zs, s4.z * 16777216.0f + Zs,
-                               s4.w * 1048576.0f + Zs);
-        // Ls == 0: the row saw no token in this range.  A NaN Ls (a NaN key
-        // or scale the row can see) propagates to the output.
-        if (a.nsplit == 1) {
-            const int n = rr / a.G, g = rr % a.G;
-            const float inv = (Ls != 0.0f) ? 1.0f / Ls : __builtin_nanf("");
-            o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-            *reinterpret_cast<float4 *>(a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD + d) = o;
-        } else {
-            const float inv = (Ls != 0.0f) ? 1.0f / Ls : 0.0f;
-            o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-            *reinterpret_cast<float4 *>(a.part_o + (pbase + rr) * kD + d) = o;
-            if (d == 0)
-                a.part_ml[pbase + rr] = make_float2(rstat[rr * 3 + 2], Ls);
+            for (int j = 0; j < 4; ++j)
+                O[j][dt] = o[j];
         }
     }
+
+    // ------------------------------------------- output or partial state
+    // One key range: the output row (NaN when no token was visible).  Several:
+    // the normalised partial output and its (max, sum) go to the workspace,
+    // where combine_kernel merges the ranges.
+    float *dst;
+    if (a.nsplit == 1) {
+        if (row >= a.R)
+            return;
+        const int n = row_token(row), g = row - n * a.G;
+        dst = a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
+        if (Ls == 0.0f) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    O[j][k] = __builtin_nanf("");
+        }
+    } else {
+        const size_t slot = ((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP + lrow;
+        dst = a.part_o + slot * kD;
+        if (wave == 0 && h == 0)
+            a.part_ml[slot] = make_float2(M, Ls);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(dst + 4 * (8 * wave + 4 * h + j)) = make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
 }
 
-// Merge of the key-range partitions of each (b, hk): out = sum_s w_s O_s /
-// sum_s w_s with w_s = exp2(m_s - max_s m_s) * l_s.  One 32-lane group per
-// (unit, row), one float4 of the row per lane; every lane loads the row's
-// (m, l) pairs and its own partial float4s in one batch, so the kernel costs
-// a single round trip to memory.  Ranges whose softmax sum is exactly 0 saw
-// no token and get weight 0; a NaN sum is kept so that it reaches the output.
+// Merge of the key ranges of each (b, hk, row tile): out = sum_s w_s O_s /
+// sum_s w_s with w_s = exp2(m_s - max_s m_s) * l_s, in a fixed order.  One
+// 32-lane group per row, one float4 of the row per lane; every lane loads
+// the row's (m, l) pairs and its own partial float4s in one batch, so the
+// kernel costs a single round trip to memory.  Ranges whose softmax sum is
+// exactly 0 saw no token and get weight 0; a NaN sum reaches the output.
+// Blocks are dealt to the XCDs like the verify work-groups of the same
+// rows, so the partial states are read where they were written.
 constexpr int kCombineChunk = 16;
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
+__global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
 {
-    const int grp = blockIdx.x * 8 + (threadIdx.x >> 5);
-    if (grp >= a.B * a.Hk * a.R)
+    int blk = blockIdx.x;
+    if ((gridDim.x & 7) == 0)
+        blk = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int grp = blk >> 2;                          // (unit, row tile)
+    const int lrow = ((blk & 3) << 3) + (threadIdx.x >> 5); // row within the tile
+    const int unit = grp / a.nrt, rt = grp % a.nrt;
+    const int row = 32 * rt + lrow;
+    if (unit >= a.B * a.Hk || row >= a.R)
         return;
-    const int unit = grp / a.R, rr = grp % a.R;
     const int d = (threadIdx.x & 31) * 4;
-    const size_t base = (size_t)unit * a.nsplit * a.R + rr;
+    const size_t base = (size_t)grp * a.nsplit * 32 + lrow;
     float M = -__builtin_inff(), den = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < a.nsplit; s0 += kCombineChunk) {
@@ -885,7 +925,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j) {
             if (s0 + j < a.nsplit) {
-                const size_t ix = base + (size_t)(s0 + j) * a.R;
+                const size_t ix = base + (size_t)(s0 + j) * 32;
                 ml[j] = a.part_ml[ix];
                 v[j] = *reinterpret_cast<const float4 *>(a.part_o + ix * kD + d);
             } else {
@@ -910,43 +950,39 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
         for (int j = 0; j < kCombineChunk; ++j) {
             const float w = (ml[j].y != 0.0f) ? __builtin_amdgcn_exp2f(ml[j].x - M) * ml[j].y : 0.0f;
             den += w;
-            acc.x += w * v[j].x;
-            acc.y += w * v[j].y;
-            acc.z += w * v[j].z;
-            acc.w += w * v[j].w;
+            acc.x = __builtin_fmaf(w, v[j].x, acc.x);
+            acc.y = __builtin_fmaf(w, v[j].y, acc.y);
+            acc.z = __builtin_fmaf(w, v[j].z, acc.z);
+            acc.w = __builtin_fmaf(w, v[j].w, acc.w);
         }
     }
     const float inv = (den != 0.0f) ? 1.0f / den : __builtin_nanf("");
     const int b = unit / a.Hk, hk = unit % a.Hk;
-    const int n = rr / a.G, g = rr % a.G;
+    const int n = (int)(((float)row + 0.5f) * __builtin_amdgcn_rcpf((float)a.G)), g = row - n * a.G;
     *reinterpret_cast<float4 *>(a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD + d) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
+
 
 } // namespace
 
 hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit)), block(256);
-    if (preset == kPresetK3V4) {
-        if (nqt == 1)
-            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 2>), grid, block, 0, s, a);
-    } else {
-        if (nqt == 1)
-            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 2>), grid, block, 0, s, a);
+    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * a.nrt)), block(256);
+    if (nqt != 1)
+        return hipErrorInvalidValue;
+    if (preset == kPresetK3V4)
+        hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1>), grid, block, 0, s, a);
+    if (hipGetLastError() != hipSuccess)
+        return hipErrorLaunchFailure;
+    if (a.nsplit > 1) {
+        // 4 blocks of 8 rows per (unit, row tile)
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hk * a.nrt * 4)), dim3(256), 0, s, a);
+        return hipGetLastError();
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
-{
-    const dim3 grid((unsigned)((a.B * a.Hk * a.R + 7) / 8)), block(256);
-    hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, a);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 } // namespace tqkv
