@@ -867,31 +867,44 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     }
 
     // ------------------------------------------- output or partial state
-    // One key range: the output row (NaN when no token was visible).  Several:
-    // the normalised partial output and its (max, sum) go to the workspace,
-    // where combine_kernel merges the ranges.
-    float *dst;
-    if (a.nsplit == 1) {
-        if (row >= a.R)
-            return;
-        const int n = row_token(row), g = row - n * a.G;
-        dst = a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
-        if (Ls == 0.0f) {
+    // One key range: the output rows (NaN where no token was visible).
+    // Several: the normalised partial outputs and their (max, sum) go to the
+    // workspace, where combine_kernel merges the ranges.  The rows are
+    // transposed through LDS so that every store instruction writes whole
+    // 512-byte rows (full cache lines) instead of 16-byte pieces of 32 rows.
+    constexpr int kOStride = kD + 4; // floats per LDS row (bank spread)
+    if (a.nsplit > 1 && wave == 0 && h == 0)
+        a.part_ml[((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP + lrow] = make_float2(M, Ls);
+    if (a.nsplit == 1 && Ls == 0.0f) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    O[j][k] = __builtin_nanf("");
-        }
-    } else {
-        const size_t slot = ((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP + lrow;
-        dst = a.part_o + slot * kD;
-        if (wave == 0 && h == 0)
-            a.part_ml[slot] = make_float2(M, Ls);
+            for (int k = 0; k < 4; ++k)
+                O[j][k] = __builtin_nanf("");
     }
+    __syncthreads(); // every wavefront has read the merge buffer
+    float *ob = reinterpret_cast<float *>(lds); // [32 rows][kOStride]
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4 *>(dst + 4 * (8 * wave + 4 * h + j)) = make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
+        *reinterpret_cast<float4 *>(ob + lrow * kOStride + 4 * (8 * wave + 4 * h + j)) =
+            make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RP * kD / 4 / 256; ++k) {
+        const int f4 = threadIdx.x + 256 * k; // float4 index, row-major
+        const int r = f4 >> 5, c = (f4 & 31) * 4;
+        const int grow = row0 + r;
+        if (grow >= a.R)
+            continue;
+        float *dst;
+        if (a.nsplit == 1) {
+            const int n = row_token(grow), g = grow - n * a.G;
+            dst = a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
+        } else {
+            dst = a.part_o + (((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP + r) * kD;
+        }
+        *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
+    }
 }
 
 // Merge of the key ranges of each (b, hk, row tile): out = sum_s w_s O_s /
