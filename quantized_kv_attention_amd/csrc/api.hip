@@ -95,7 +95,7 @@ size_t workspace_for(const tqkv_cache *c, int n_spec, int Hq, int splits)
         return 0;
     const size_t groups = (size_t)c->B * c->Hk * row_tiles((Hq / c->Hk) * n_spec);
     const size_t slots = groups * splits * 32;
-    return slots * TQKV_HEAD_DIM * sizeof(float) + slots * 2 * sizeof(float);
+    return slots * 2 * sizeof(float) + slots * TQKV_HEAD_DIM * sizeof(uint16_t);
 }
 
 } // namespace
@@ -218,9 +218,10 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
     a.seq_lens = seq_lens;
     a.out = out;
     const size_t groups = (size_t)cache->B * cache->Hk * row_tiles(R);
-    float *part = splits > 1 ? static_cast<float *>(workspace) : nullptr;
-    a.part_o = part;
-    a.part_ml = splits > 1 ? reinterpret_cast<float2 *>(part + groups * splits * 32 * TQKV_HEAD_DIM) : nullptr;
+    // workspace: (max, sum) pairs first (8-byte aligned), then the binary16 outputs
+    const size_t slots = groups * splits * 32;
+    a.part_ml = splits > 1 ? static_cast<float2 *>(workspace) : nullptr;
+    a.part_o = splits > 1 ? reinterpret_cast<_Float16 *>(static_cast<uint8_t *>(workspace) + slots * sizeof(float2)) : nullptr;
     a.qscale = scale * 1.4426950408889634f;
     a.q_f16 = (q_dtype == TQKV_Q_F16);
     a.Hk = cache->Hk;

@@ -65,7 +65,7 @@ struct VerifyArgs {
     const int32_t *seq_lens;
     float *out;      // [N, B, Hq, 128]
     // partial states of the key ranges (nsplit > 1), per (unit, row tile) g:
-    float *part_o;   // [g][nsplit][32 rows][128] normalised partial outputs
+    _Float16 *part_o; // [g][nsplit][32 rows][128] normalised partial outputs (binary16)
     float2 *part_ml; // [g][nsplit][32 rows] (running max in log2 units, softmax sum)
     float qscale;       // softmax scale * log2(e)
     int q_f16;

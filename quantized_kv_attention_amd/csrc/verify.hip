@@ -868,8 +868,11 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
 
     // ------------------------------------------- output or partial state
     // One key range: the output rows (NaN where no token was visible).
-    // Several: the normalised partial outputs and their (max, sum) go to the
-    // workspace, where combine_kernel merges the ranges.  The rows are
+    // Several: the normalised partial outputs (binary16, saturated to the
+    // finite range, NaN kept) and their (max, sum) go to the workspace, where
+    // combine_kernel merges the ranges.  A normalised partial output is a
+    // convex combination of dequantised values, so binary16 keeps it to
+    // 2^-11 relative.  The rows are
     // transposed through LDS so that every store instruction writes whole
     // 512-byte rows (full cache lines) instead of 16-byte pieces of 32 rows.
     constexpr int kOStride = kD + 4; // floats per LDS row (bank spread)
@@ -889,21 +892,38 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         *reinterpret_cast<float4 *>(ob + lrow * kOStride + 4 * (8 * wave + 4 * h + j)) =
             make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
     __syncthreads();
+    if (a.nsplit == 1) {
 #pragma unroll
-    for (int k = 0; k < RP * kD / 4 / 256; ++k) {
-        const int f4 = threadIdx.x + 256 * k; // float4 index, row-major
-        const int r = f4 >> 5, c = (f4 & 31) * 4;
-        const int grow = row0 + r;
-        if (grow >= a.R)
-            continue;
-        float *dst;
-        if (a.nsplit == 1) {
+        for (int k = 0; k < RP * kD / 4 / 256; ++k) {
+            const int f4 = threadIdx.x + 256 * k; // float4 index, row-major
+            const int r = f4 >> 5, c = (f4 & 31) * 4;
+            const int grow = row0 + r;
+            if (grow >= a.R)
+                continue;
             const int n = row_token(grow), g = grow - n * a.G;
-            dst = a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
-        } else {
-            dst = a.part_o + (((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP + r) * kD;
+            float *dst = a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
+            *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
         }
-        *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
+    } else {
+        _Float16 *pbase = a.part_o + ((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP * kD;
+#pragma unroll
+        for (int k = 0; k < RP * kD / 8 / 256; ++k) {
+            const int e8 = threadIdx.x + 256 * k; // 8-element chunk, row-major
+            const int r = e8 >> 4, c = (e8 & 15) * 8;
+            const float4 x0 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
+            const float4 x1 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float p = fminf(fmaxf(xs[2 * i], -65504.0f), 65504.0f);
+                float q = fminf(fmaxf(xs[2 * i + 1], -65504.0f), 65504.0f);
+                p = (xs[2 * i] == xs[2 * i]) ? p : xs[2 * i];
+                q = (xs[2 * i + 1] == xs[2 * i + 1]) ? q : xs[2 * i + 1];
+                w[i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)q});
+            }
+            *reinterpret_cast<u32x4 *>(pbase + r * kD + c) = u32x4{w[0], w[1], w[2], w[3]};
+        }
     }
 }
 
@@ -940,7 +960,9 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
             if (s0 + j < a.nsplit) {
                 const size_t ix = base + (size_t)(s0 + j) * 32;
                 ml[j] = a.part_ml[ix];
-                v[j] = *reinterpret_cast<const float4 *>(a.part_o + ix * kD + d);
+                const uint2 hv = *reinterpret_cast<const uint2 *>(a.part_o + ix * kD + d);
+                const half2_t h0 = __builtin_bit_cast(half2_t, hv.x), h1 = __builtin_bit_cast(half2_t, hv.y);
+                v[j] = make_float4((float)h0[0], (float)h0[1], (float)h1[0], (float)h1[1]);
             } else {
                 ml[j] = make_float2(-__builtin_inff(), 0.0f);
                 v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
