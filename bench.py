@@ -134,6 +134,9 @@ def main():
     si, po = synth.token_lists(B, S, S - N, S)
     Kn = to_dev(synth.rows(inp["K"], S - N, S), dev)
     Vn = to_dev(synth.rows(inp["V"], S - N, S), dev)
+    # the same new tokens as [N, B, Hk, 128] for the fused store + verify call
+    Kf = to_dev(np.ascontiguousarray(inp["K"][:, S - N:S].transpose(1, 0, 2, 3)), dev)
+    Vf = to_dev(np.ascontiguousarray(inp["V"][:, S - N:S].transpose(1, 0, 2, 3)), dev)
     si_d, po_d = to_dev(si, dev), to_dev(po, dev)
     Q = to_dev(inp["Q"], dev)
     sl = to_dev(inp["seq_lens"], dev)
@@ -154,6 +157,10 @@ def main():
     def step(i):
         store(i)
         verify(i)
+
+    def step_fused(i):
+        tq.tqkv_store_verify(caches[i % R], Kf, Vf, Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
+                             out=out, workspace=ws)
 
     def capture(fn, n, offset=0):
         g = torch.cuda.CUDAGraph()
@@ -183,6 +190,7 @@ def main():
     g_steps = capture(step, args.steps)
     g_verify = capture(verify, args.kernel_calls)
     g_store = capture(store, args.kernel_calls)
+    g_fused = capture(step_fused, args.kernel_calls)
     g_warm.replay()
     torch.cuda.synchronize()
 
@@ -198,6 +206,7 @@ def main():
     # per-launch durations with HIP events on the launch stream
     verify_ms = min(time_graph(g_verify) for _ in range(3)) / args.kernel_calls
     store_ms = min(time_graph(g_store) for _ in range(3)) / args.kernel_calls
+    fused_ms = min(time_graph(g_fused) for _ in range(3)) / args.kernel_calls
     # warm (MALL-resident) verify: one replica only
     g_warmv = capture(lambda i: verify(0), args.kernel_calls)
     verify_warm_ms = min(time_graph(g_warmv) for _ in range(3)) / args.kernel_calls
@@ -238,12 +247,13 @@ def main():
                            cfg["causal"]),
             "num_splits": splits,
             "cold_replicas": R,
-            "step": "store(N_spec new tokens x B x Hk) + verify(all tokens)",
+            "step": "tqkv_store(N_spec new tokens x B x Hk) + tqkv_verify(all tokens)",
             "timing": "HIP graph of K steps, one replay",
         },
         "us_per_step": round(ms_per_step * 1e3, 3),
         "us_per_verify_call": round(verify_ms * 1e3, 3),
         "us_per_store_call": round(store_ms * 1e3, 3),
+        "us_per_step_fused_store_verify": round(fused_ms * 1e3, 3),
         "us_per_verify_call_mall_warm": round(verify_warm_ms * 1e3, 3),
         "us_per_step_eager": round(eager_ms * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,
@@ -254,7 +264,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(args.workload),
-            "kernel": "tqkv_verify (verify_kernel + combine_kernel when splits > 1)",
+            "kernel": "tqkv_verify: verify_kernel (+ combine_kernel when splits > 1)",
             "bytes_per_launch": kv_bytes + qo_bytes,
         },
         "cpu_baseline": cpu,

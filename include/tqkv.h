@@ -145,6 +145,22 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
                 int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* store + verify in one launch, for the speculative-decode step of the
+ * pages' Part 4 (the N_spec draft tokens are written to the cache, then
+ * their queries attend to it):
+ *   K, V      device, fp16 [n_spec, B, Hk, 128], 2-byte aligned: token n of
+ *             sequence b is quantised into position seq_lens[b] - n_spec + n
+ *             (exactly the bytes tqkv_store writes for it)
+ *   the other arguments and the result are those of tqkv_verify.
+ * Equivalent to tqkv_store of those n_spec * B tokens followed by
+ * tqkv_verify, without the separate store launch; the work-groups that read
+ * the new tokens' tiles quantise them first.  Same preconditions as
+ * tqkv_verify, plus n_spec <= seq_lens[b].
+ * Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_store_verify(const tqkv_cache *cache, const void *K, const void *V, const void *Q, int q_dtype,
+                      const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
+                      float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *tqkv_status_string(int status);
 

@@ -15,6 +15,7 @@ Names mirror the C entry points::
     tqkv_verify_num_splits(cache, n_spec, Hq, num_splits)
     tqkv_verify_workspace_bytes(cache, n_spec, Hq, num_splits)
     tqkv_verify(cache, Q, seq_lens, n_spec, Hq, causal, ...)
+    tqkv_store_verify(cache, K, V, Q, seq_lens, n_spec, Hq, causal, ...)
     tqkv_status_string(status)              tqkv_version()
 
 ``Cache`` owns a device buffer and the descriptor the C calls take.
@@ -29,7 +30,7 @@ import torch
 __all__ = [
     "K8V4", "K3V4_NC", "HEAD_DIM", "BLOCK_TOKENS", "TqkvError", "Cache", "library_path",
     "tqkv_slot_bytes", "tqkv_block_bytes", "tqkv_cache_bytes", "tqkv_store",
-    "tqkv_verify_num_splits", "tqkv_verify_workspace_bytes", "tqkv_verify",
+    "tqkv_verify_num_splits", "tqkv_verify_workspace_bytes", "tqkv_verify", "tqkv_store_verify",
     "tqkv_status_string", "tqkv_version",
 ]
 
@@ -84,6 +85,8 @@ def _load():
     L.tqkv_verify_workspace_bytes.restype = I
     L.tqkv_verify.argtypes = [D, P, I, P, I, I, I, I, ctypes.c_float, P, P, S, P]
     L.tqkv_verify.restype = I
+    L.tqkv_store_verify.argtypes = [D, P, P, P, I, P, I, I, I, I, ctypes.c_float, P, P, S, P]
+    L.tqkv_store_verify.restype = I
     L.tqkv_status_string.argtypes = [I]
     L.tqkv_status_string.restype = ctypes.c_char_p
     L.tqkv_version.argtypes = []
@@ -189,11 +192,8 @@ def tqkv_verify_workspace_bytes(cache: Cache, n_spec: int, Hq: int, num_splits: 
     return int(n.value)
 
 
-def tqkv_verify(cache: Cache, Q: torch.Tensor, seq_lens: torch.Tensor, n_spec: int, Hq: int,
-                causal: bool, num_splits: int = 0, sm_scale: float = 0.0,
-                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                stream=None) -> torch.Tensor:
-    """Verification attention; returns ``out`` (fp32 [n_spec, B, Hq, 128])."""
+def _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, workspace):
+    """Argument checks and defaults shared by tqkv_verify and tqkv_store_verify."""
     if Q.dtype == torch.float32:
         qd = Q_F32
     elif Q.dtype == torch.float16:
@@ -213,8 +213,39 @@ def tqkv_verify(cache: Cache, Q: torch.Tensor, seq_lens: torch.Tensor, n_spec: i
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return qd, out, ws_ptr, ws_len
+
+
+def tqkv_verify(cache: Cache, Q: torch.Tensor, seq_lens: torch.Tensor, n_spec: int, Hq: int,
+                causal: bool, num_splits: int = 0, sm_scale: float = 0.0,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """Verification attention; returns ``out`` (fp32 [n_spec, B, Hq, 128])."""
+    qd, out, ws_ptr, ws_len = _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, workspace)
     st = _load().tqkv_verify(ctypes.byref(cache.desc), Q.data_ptr(), qd, seq_lens.data_ptr(), n_spec,
                              Hq, int(bool(causal)), num_splits, float(sm_scale), out.data_ptr(),
                              ws_ptr, ws_len, _stream_ptr(Q, stream))
     _check(st, "tqkv_verify")
+    return out
+
+
+def tqkv_store_verify(cache: Cache, K: torch.Tensor, V: torch.Tensor, Q: torch.Tensor, seq_lens: torch.Tensor,
+                      n_spec: int, Hq: int, causal: bool, num_splits: int = 0, sm_scale: float = 0.0,
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Store the n_spec new tokens of every sequence (K, V fp16 [n_spec, B, Hk, 128];
+    token n of sequence b goes to position seq_lens[b] - n_spec + n) and run the
+    verification attention in one launch; returns ``out``."""
+    shape = (n_spec, cache.B, cache.Hk, HEAD_DIM)
+    if K.dtype != torch.float16 or V.dtype != torch.float16:
+        raise TypeError("K and V must be float16")
+    if K.shape != shape or V.shape != shape or not K.is_contiguous() or not V.is_contiguous():
+        raise ValueError("K and V must be contiguous [n_spec, B, Hk, 128] tensors")
+    if K.device != cache.buffer.device or V.device != cache.buffer.device:
+        raise ValueError("K and V must be on the cache's device")
+    qd, out, ws_ptr, ws_len = _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, workspace)
+    st = _load().tqkv_store_verify(ctypes.byref(cache.desc), K.data_ptr(), V.data_ptr(), Q.data_ptr(), qd,
+                                   seq_lens.data_ptr(), n_spec, Hq, int(bool(causal)), num_splits,
+                                   float(sm_scale), out.data_ptr(), ws_ptr, ws_len, _stream_ptr(Q, stream))
+    _check(st, "tqkv_store_verify")
     return out

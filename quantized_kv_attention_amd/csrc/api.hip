@@ -100,6 +100,76 @@ size_t workspace_for(const tqkv_cache *c, int n_spec, int Hq, int splits)
 
 } // namespace
 
+namespace {
+int verify_impl(const tqkv_cache *cache, const void *Knew, const void *Vnew, const void *Q, int q_dtype,
+                       const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
+                       float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = check_verify_shape(cache, n_spec, Hq);
+    if (st != TQKV_OK)
+        return st;
+    if (!Q || !seq_lens || !out || num_splits < 0)
+        return TQKV_ERR_ARG;
+    if ((Knew == nullptr) != (Vnew == nullptr))
+        return TQKV_ERR_ARG;
+    if (Knew && (!aligned(Knew, 2) || !aligned(Vnew, 2)))
+        return TQKV_ERR_ALIGN;
+    if (q_dtype != TQKV_Q_F32 && q_dtype != TQKV_Q_F16)
+        return TQKV_ERR_ARG;
+    if (causal != 0 && causal != 1)
+        return TQKV_ERR_ARG;
+    if (!(sm_scale >= 0.0f) || isinf(sm_scale))
+        return TQKV_ERR_ARG;
+    if (!aligned(Q, 16) || !aligned(seq_lens, 4) || !aligned(out, 16))
+        return TQKV_ERR_ALIGN;
+    int cus = current_device_cus();
+    if (cus < 0)
+        return cus;
+    const int splits = plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec);
+    const size_t need = workspace_for(cache, n_spec, Hq, splits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return TQKV_ERR_WORKSPACE;
+        if (!aligned(workspace, 256))
+            return TQKV_ERR_ALIGN;
+    }
+    const int G = Hq / cache->Hk;
+    const int R = G * n_spec;
+    const float scale = (sm_scale == 0.0f) ? 0.08838834764831845f : sm_scale;
+    VerifyArgs a;
+    a.base = static_cast<const uint8_t *>(cache->base);
+    a.Q = Q;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    const size_t groups = (size_t)cache->B * cache->Hk * row_tiles(R);
+    // workspace: (max, sum) pairs first (8-byte aligned), then the binary16 outputs
+    const size_t slots = groups * splits * 32;
+    a.part_ml = splits > 1 ? static_cast<float2 *>(workspace) : nullptr;
+    a.part_o = splits > 1 ? reinterpret_cast<_Float16 *>(static_cast<uint8_t *>(workspace) + slots * sizeof(float2)) : nullptr;
+    a.qscale = scale * 1.4426950408889634f;
+    a.q_f16 = (q_dtype == TQKV_Q_F16);
+    a.Hk = cache->Hk;
+    a.max_seq = cache->max_seq;
+    a.nblk = nblocks(cache->max_seq);
+    a.B = cache->B;
+    a.N = n_spec;
+    a.Hq = Hq;
+    a.G = G;
+    a.R = R;
+    a.causal = causal;
+    a.nsplit = splits;
+    a.nrt = row_tiles(R);
+    a.Knew = static_cast<const uint16_t *>(Knew);
+    a.Vnew = static_cast<const uint16_t *>(Vnew);
+    a.wbase = static_cast<uint8_t *>(cache->base);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_verify(cache->preset, 1, a, s) != hipSuccess)
+        return TQKV_ERR_LAUNCH;
+    return TQKV_OK;
+}
+
+} // namespace
+
 extern "C" {
 
 size_t tqkv_slot_bytes(int preset)
@@ -185,60 +255,18 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
                 int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
                 void *workspace, size_t workspace_bytes, void *stream)
 {
-    int st = check_verify_shape(cache, n_spec, Hq);
-    if (st != TQKV_OK)
-        return st;
-    if (!Q || !seq_lens || !out || num_splits < 0)
+    return verify_impl(cache, nullptr, nullptr, Q, q_dtype, seq_lens, n_spec, Hq, causal, num_splits, sm_scale, out,
+                       workspace, workspace_bytes, stream);
+}
+
+int tqkv_store_verify(const tqkv_cache *cache, const void *K, const void *V, const void *Q, int q_dtype,
+                      const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
+                      float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!K || !V)
         return TQKV_ERR_ARG;
-    if (q_dtype != TQKV_Q_F32 && q_dtype != TQKV_Q_F16)
-        return TQKV_ERR_ARG;
-    if (causal != 0 && causal != 1)
-        return TQKV_ERR_ARG;
-    if (!(sm_scale >= 0.0f) || isinf(sm_scale))
-        return TQKV_ERR_ARG;
-    if (!aligned(Q, 16) || !aligned(seq_lens, 4) || !aligned(out, 16))
-        return TQKV_ERR_ALIGN;
-    int cus = current_device_cus();
-    if (cus < 0)
-        return cus;
-    const int splits = plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec);
-    const size_t need = workspace_for(cache, n_spec, Hq, splits);
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need)
-            return TQKV_ERR_WORKSPACE;
-        if (!aligned(workspace, 256))
-            return TQKV_ERR_ALIGN;
-    }
-    const int G = Hq / cache->Hk;
-    const int R = G * n_spec;
-    const float scale = (sm_scale == 0.0f) ? 0.08838834764831845f : sm_scale;
-    VerifyArgs a;
-    a.base = static_cast<const uint8_t *>(cache->base);
-    a.Q = Q;
-    a.seq_lens = seq_lens;
-    a.out = out;
-    const size_t groups = (size_t)cache->B * cache->Hk * row_tiles(R);
-    // workspace: (max, sum) pairs first (8-byte aligned), then the binary16 outputs
-    const size_t slots = groups * splits * 32;
-    a.part_ml = splits > 1 ? static_cast<float2 *>(workspace) : nullptr;
-    a.part_o = splits > 1 ? reinterpret_cast<_Float16 *>(static_cast<uint8_t *>(workspace) + slots * sizeof(float2)) : nullptr;
-    a.qscale = scale * 1.4426950408889634f;
-    a.q_f16 = (q_dtype == TQKV_Q_F16);
-    a.Hk = cache->Hk;
-    a.max_seq = cache->max_seq;
-    a.nblk = nblocks(cache->max_seq);
-    a.B = cache->B;
-    a.N = n_spec;
-    a.Hq = Hq;
-    a.G = G;
-    a.R = R;
-    a.causal = causal;
-    a.nsplit = splits;
-    a.nrt = row_tiles(R);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_verify(cache->preset, 1, a, s) != hipSuccess)
-        return TQKV_ERR_LAUNCH;
-    return TQKV_OK;
+    return verify_impl(cache, K, V, Q, q_dtype, seq_lens, n_spec, Hq, causal, num_splits, sm_scale, out, workspace,
+                       workspace_bytes, stream);
 }
 
 const char *tqkv_status_string(int status)

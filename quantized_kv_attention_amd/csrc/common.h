@@ -72,6 +72,11 @@ struct VerifyArgs {
     int Hk, max_seq, nblk;
     int B, N, Hq, G, R, causal, nsplit;
     int nrt; // row tiles per (b, hk): one work-group each
+    // fused store (null for a plain verify): the n_spec new tokens of every
+    // sequence, fp16 [N, B, Hk, 128]; token n of sequence b goes to position
+    // seq_lens[b] - N + n of the cache before it is attended to
+    const uint16_t *Knew, *Vnew;
+    uint8_t *wbase; // the cache, writable (== base)
 };
 
 // Launchers (defined next to their kernels).

@@ -1,0 +1,228 @@
+// Quantisation of one token-head into the packed cache, shared by the store
+// kernel and the fused store + verify kernel.
+//
+// Method (Context and Part 6 of "Speculative decoding on Intel Arc:
+// TurboQuant KV + a fused N_spec kernel"): keys are rotated by a
+// Walsh-Hadamard transform and coded with a precomputed Lloyd-Max codebook
+// plus a norm correction (k3v4_nc), or kept as FP8 E4M3 codes (k8v4); values
+// get uniform 4-bit codes with a scale and a zero.
+//
+// One wavefront quantises one token-head (128 coordinates): lane l holds
+// coordinates l and l + 64, so the last WHT stage and the first step of the
+// stride-halving sum are in-lane and every other step is an xor-shuffle.
+// IEEE add is commutative, so the xor-butterfly reductions reproduce the
+// stride-halving tree bit for bit, and the WHT butterflies take the same
+// operands in the same stage order h = 1, 2, ..., 64 as the specification.
+// All arithmetic is binary32 with explicit round-to-nearest-even intrinsics
+// (no contraction), because the codes are integers decided in binary32 and
+// must be bit-exact.
+#pragma once
+#include "codebook.h"
+#include "common.h"
+
+namespace tqkv {
+namespace quant {
+
+__device__ inline float h2f_q(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// Correctly rounded binary32 square root (llvm.sqrt.f32 is lowered to
+// v_sqrt_f32 plus a one-ulp residual correction; HIP's __fsqrt_rn maps to the
+// uncorrected native instruction).
+__device__ inline float sqrt_rn(float x) { return __builtin_sqrtf(x); }
+
+// binary32 -> binary16 bits, RNE; NaN becomes the canonical 0x7E00.
+__device__ inline uint16_t f2h(float f)
+{
+    if (f != f)
+        return 0x7E00;
+    return __half_as_ushort(__float2half_rn(f));
+}
+
+__device__ inline float centroid(int c)
+{
+    // select chain over the 8 constant levels (keeps the table in immediates)
+    float lo = (c & 2) ? ((c & 1) ? kCentroid[3] : kCentroid[2]) : ((c & 1) ? kCentroid[1] : kCentroid[0]);
+    float hi = (c & 2) ? ((c & 1) ? kCentroid[7] : kCentroid[6]) : ((c & 1) ? kCentroid[5] : kCentroid[4]);
+    return (c & 4) ? hi : lo;
+}
+
+__device__ inline int lloyd_code(float y)
+{
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+        c += (y >= kThreshold[j]) ? 1 : 0; // NaN compares false: code 0
+    return c;
+}
+
+// Sum over the wavefront of one value per lane by xor-butterflies 32..1.
+__device__ inline float wave_tree_sum(float a)
+{
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1)
+        a = __fadd_rn(a, __shfl_xor(a, s, 64));
+    return a;
+}
+
+// OCP E4M3 encoding with round-to-nearest-even on the binary32 bit pattern
+// and saturation to +-448; NaN -> 0x7F.
+__device__ inline uint32_t e4m3_rne_sat(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return 0x7Fu;
+    float af = __uint_as_float(a);
+    if (af >= 448.0f)
+        return sign | 0x7Eu;
+    if (a < 0x3C800000u) { // below 2^-6: multiples of 2^-9
+        float q = rintf(__fmul_rn(af, 512.0f));
+        return sign | (uint32_t)q;
+    }
+    int e = (int)(a >> 23) - 127 + 7;      // biased e4m3 exponent, 1..15
+    uint32_t keep = (a >> 20) & 7u;        // top three mantissa bits
+    uint32_t rest = a & 0xFFFFFu;          // the 20 bits rounded away
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u)))
+        keep += 1;
+    if (keep == 8u) {
+        keep = 0;
+        e += 1;
+    }
+    uint32_t code = ((uint32_t)e << 3) | keep;
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+
+// One token-head's inputs as this lane holds them: coordinates lane and
+// lane + 64 of the key and of the value (fp16 bit patterns).
+struct TokenHead {
+    uint16_t k0, k1, v0, v1;
+};
+
+__device__ inline TokenHead load_token_head(const uint16_t *kp, const uint16_t *vp, int lane)
+{
+    return TokenHead{kp[lane], kp[lane + 64], vp[lane], vp[lane + 64]};
+}
+
+// Quantise a loaded token-head into token slot tb of the 16-token cache
+// block blk.  Called by all 64 lanes of one wavefront.
+template <int PRESET>
+__device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead &in, int lane)
+{
+    using L = Layout<PRESET>;
+    // ---------------------------------------------------------------- keys
+    float x0 = h2f_q(in.k0), x1 = h2f_q(in.k1);
+    if constexpr (PRESET == kPresetK3V4) {
+        const float n = sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(x0, x0), __fmul_rn(x1, x1))));
+#pragma unroll
+        for (int h = 1; h < 64; h <<= 1) {
+            float p0 = __shfl_xor(x0, h, 64), p1 = __shfl_xor(x1, h, 64);
+            if (lane & h) {
+                x0 = __fsub_rn(p0, x0);
+                x1 = __fsub_rn(p1, x1);
+            } else {
+                x0 = __fadd_rn(x0, p0);
+                x1 = __fadd_rn(x1, p1);
+            }
+        }
+        {
+            float u = x0, v = x1;
+            x0 = __fadd_rn(u, v);
+            x1 = __fsub_rn(u, v);
+        }
+        const float r = __fdiv_rn(1.0f, __fmul_rn(sqrt_rn(128.0f), n));
+        const int c0 = lloyd_code(__fmul_rn(x0, r));
+        const int c1 = lloyd_code(__fmul_rn(x1, r));
+        const float q0 = centroid(c0), q1 = centroid(c1);
+        const float gam = __fdiv_rn(1.0f, sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(q0, q0), __fmul_rn(q1, q1)))));
+
+        // Bit placement: coordinate d = 64h + 32g + 8k + e -> dword triple
+        // 6h+3g+{0,1,2}, byte lane e%4, slot 2k + e/4.  Slots 0-5 hold all
+        // three bits at word slot/2, offset 3*(slot%2); slots 6 and 7 keep
+        // bits 0-1 at offset 6 of word slot-6 and bit 2 at offset slot of
+        // word 2.  Lane l carries d = l (h = 0) and d = l + 64 (h = 1), both
+        // in triple g = l/32 of their half.
+        uint32_t w[2][3] = {{0, 0, 0}, {0, 0, 0}};
+        {
+            const int k = (lane >> 3) & 3, e = lane & 7;
+            const int sl = 2 * k + (e >> 2), sh = 8 * (e & 3);
+            const uint32_t cc[2] = {(uint32_t)c0, (uint32_t)c1};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if (sl < 6) {
+                    w[hh][sl >> 1] |= cc[hh] << (sh + 3 * (sl & 1));
+                } else {
+                    w[hh][sl - 6] |= (cc[hh] & 3u) << (sh + 6);
+                    w[hh][2] |= (cc[hh] >> 2) << (sh + sl);
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 1; s < 32; s <<= 1)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    w[hh][j] |= __shfl_xor(w[hh][j], s, 64);
+        if ((lane & 31) == 0) {
+            const int g = lane >> 5;
+            uint32_t *kd = reinterpret_cast<uint32_t *>(blk + tb * L::kKeyBytesPerToken);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                kd[3 * g + j] = w[0][j];
+                kd[6 + 3 * g + j] = w[1][j];
+            }
+        }
+        if (lane == 0)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = f2h(n);
+        if (lane == 1)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta1 + 2 * tb) = f2h(gam);
+    } else {
+        float amax = fmaxf(fmaxf(0.0f, fabsf(x0)), fabsf(x1));
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+        const uint16_t sh = f2h(__fdiv_rn(amax, 448.0f));
+        const float s = h2f_q(sh);
+        const uint32_t c0 = (s == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x0, s));
+        const uint32_t c1 = (s == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x1, s));
+        uint8_t *kd = blk + tb * L::kKeyBytesPerToken;
+        kd[lane] = (uint8_t)c0;
+        kd[lane + 64] = (uint8_t)c1;
+        if (lane == 0)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = sh;
+    }
+
+    // -------------------------------------------------------------- values
+    const float v0 = h2f_q(in.v0), v1 = h2f_q(in.v1);
+    float mn = fminf(fminf(__int_as_float(0x7F800000), v0), v1);
+    float mx = fmaxf(fmaxf(__int_as_float(0xFF800000), v0), v1);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, s, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+    }
+    const uint16_t zh = f2h(__fadd_rn(mn, 0.0f)); // -0 -> +0
+    const float zero = h2f_q(zh);
+    const uint16_t sch = f2h(__fdiv_rn(__fsub_rn(mx, mn), 15.0f));
+    const float sc = h2f_q(sch);
+    auto vcode = [&](float v) -> uint32_t {
+        if (sc == 0.0f)
+            return 0u;
+        float q = rintf(__fdiv_rn(__fsub_rn(v, zero), sc));
+        return (q > 0.0f) ? ((q >= 15.0f) ? 15u : (uint32_t)q) : 0u;
+    };
+    const uint32_t vc0 = vcode(v0), vc1 = vcode(v1);
+    const uint32_t o0 = __shfl_xor(vc0, 1, 64), o1 = __shfl_xor(vc1, 1, 64);
+    // even lane: byte l/2 = (d=l | d=l+1); odd lane: byte 32 + l/2 = (d=l+63 | d=l+64)
+    const int pbyte = (lane & 1) ? (32 + (lane >> 1)) : (lane >> 1);
+    const uint32_t byte = (lane & 1) ? (o1 | (vc1 << 4)) : (vc0 | (o0 << 4));
+    blk[L::kValOff + val_byte_offset(tb, pbyte)] = (uint8_t)byte;
+    if (lane == 2)
+        *reinterpret_cast<uint16_t *>(blk + L::kVScale + 2 * tb) = sch;
+    if (lane == 3)
+        *reinterpret_cast<uint16_t *>(blk + L::kVZero + 2 * tb) = zh;}
+
+} // namespace quant
+} // namespace tqkv

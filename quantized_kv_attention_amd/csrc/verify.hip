@@ -34,6 +34,7 @@
 //    than one key range per unit a second kernel merges the ranges.
 #include "codebook.h"
 #include "common.h"
+#include "quant.h"
 
 #include <type_traits>
 
@@ -485,10 +486,41 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     const uint32_t voff = 16 * lane;
     const uint32_t voff_last = (uint32_t)min(16 * lane, 2 * L_::kBlockBytes - 16 - 1024 * (LPT - 1));
     int issued = 0; // tiles of this wavefront issued so far (wave-uniform)
+    // fused store: new tokens [tn0, L) of this unit; tiles holding them are
+    // loaded only after they have been stored (step 3)
+    const int tn0 = (a.Knew != nullptr) ? L - a.N : L;
+    const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile); // this work-group's share
+    const int pre = min(kInitTiles, max(0, min(ntile, (tn0 - kt0 * kTile) / kTile)));
+    for (; issued < pre; ++issued)
+        issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + issued * kSlotBytes, voff, voff_last, lane);
+
+    // 3. Fused store: the work-group whose key range holds new tokens of
+    //    this unit quantises them into the cache first (the bytes tqkv_store
+    //    writes), spread over its four wavefronts, and waits until all of its
+    //    stores are complete before any wavefront loads a tile that holds
+    //    them.  (Work-groups of the other row tiles store the same tokens
+    //    again: identical bytes.)
+    if (wn0 < wn1) {
+        // two token-heads per wavefront at a time, both loaded up front
+        for (int t = wn0 + wave; t < wn1; t += 2 * kWaves) {
+            const int t2 = t + kWaves;
+            const size_t src = ((size_t)((t - (L - a.N)) * a.B + b) * a.Hk + hk) * kD;
+            const size_t src2 = ((size_t)((min(t2, wn1 - 1) - (L - a.N)) * a.B + b) * a.Hk + hk) * kD;
+            const quant::TokenHead x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+            const quant::TokenHead x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+            quant::quantize_token_head<PRESET>(a.wbase + ((size_t)unit * a.nblk + (t >> 4)) * L_::kBlockBytes, t & 15,
+                                               x, lane);
+            if (t2 < wn1)
+                quant::quantize_token_head<PRESET>(a.wbase + ((size_t)unit * a.nblk + (t2 >> 4)) * L_::kBlockBytes,
+                                                   t2 & 15, x2, lane);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
     for (; issued < min(kInitTiles, ntile); ++issued)
         issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + issued * kSlotBytes, voff, voff_last, lane);
 
-    // 3. state set-up while the loads are in flight
+    // 4. state set-up while the loads are in flight
     int erow[NQT]; // effective end of this lane's query rows (causal window)
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
@@ -526,7 +558,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     wait_ring<LPT>(issued); // this wavefront's query loads have landed
     lds_barrier();          // ... and every other wavefront's
 
-    // 4. scale (softmax scale * log2 e: the softmax runs in base 2) and round
+    // 5. scale (softmax scale * log2 e: the softmax runs in base 2) and round
     //    to binary16; thread t converts CPT coordinates of row t / TPR
     constexpr int CPT = 16 * NQT, TPR = kD / CPT;
     {
@@ -566,7 +598,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         lds_barrier();
     }
 
-    // 5. k3v4_nc: rotate by the normalised WHT, q' = H q / sqrt(128), as the
+    // 6. k3v4_nc: rotate by the normalised WHT, q' = H q / sqrt(128), as the
     //    MFMA product Q'^T = H Q^T; wavefront w computes output coordinates
     //    32w..32w+31 of every row and writes them back in place
     if constexpr (PRESET == kPresetK3V4) {
@@ -603,7 +635,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         lds_barrier();
     }
 
-    // 6. the QK^T B operands, held in registers for the whole key loop
+    // 7. the QK^T B operands, held in registers for the whole key loop
     half8_t QB[NQT][8];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)

@@ -109,3 +109,17 @@ def test_verify_rejects_bad_arguments():
     assert n.value == 0
     assert L.tqkv_verify_workspace_bytes(ctypes.byref(d), 8, 16, 0, None) == -1
     assert L.tqkv_verify_num_splits(ctypes.byref(d), 0, 16, 0) == 0
+
+
+def test_store_verify_rejects_bad_arguments():
+    L = tq.lib()
+    d = _desc(Hk=2)
+
+    def call(K=4096, V=4096, Q=4096, n=8):
+        return L.tqkv_store_verify(ctypes.byref(d), K, V, Q, 0, 4096, n, 16, 1, 0, 0.0, 4096, None, 0, None)
+
+    assert call(K=None) == -1
+    assert call(V=None) == -1
+    assert call(K=4097) == -3           # K must be 2-byte aligned
+    assert call(Q=None) == -1
+    assert call(n=9) == -2

@@ -229,3 +229,59 @@ def test_verify_rejects_bad_workspace():
         tq.tqkv_verify(cache, to_dev(inp["Q"]), to_dev(inp["seq_lens"]), cfg["N"], cfg["Hq"], True,
                        num_splits=3, workspace=small)
     assert e.value.status == -4
+
+
+# ------------------------------------------------------- fused store+verify ---
+
+def _token_lists_ragged(lens, start_from_end=None):
+    """(seq_idx, pos) of positions [0, lens[b]) of every sequence, or only
+    the last `start_from_end` positions of each when given."""
+    si, po = [], []
+    for b, L in enumerate(lens):
+        lo = 0 if start_from_end is None else L - start_from_end
+        si += [b] * (L - lo)
+        po += list(range(lo, L))
+    return np.array(si, np.int32), np.array(po, np.int32)
+
+
+def _rows_at(X, si, po):
+    """X[b, p] for the listed (b, p): [T, Hk, 128]."""
+    return np.ascontiguousarray(X[si, po])
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("shape", [
+    dict(N=8, B=2, Hq=16, Hk=2, S=203, lens=(196, 166), ns=0),   # 64 rows: two row tiles
+    dict(N=8, B=2, Hq=16, Hk=2, S=203, lens=(196, 166), ns=3),   # new tokens straddle key ranges / wavefronts
+    dict(N=4, B=3, Hq=8, Hk=1, S=100, lens=(100, 37, 64), ns=1),  # 32 rows, one key range
+    dict(N=8, B=1, Hq=8, Hk=1, S=8, lens=(8,), ns=0),             # the whole sequence is new
+    dict(N=1, B=2, Hq=4, Hk=1, S=50, lens=(50, 17), ns=2),        # plain decode
+], ids=lambda s: "N%d_Hq%d_Hk%d_S%d_ns%d" % (s["N"], s["Hq"], s["Hk"], s["S"], s["ns"]))
+def test_store_verify_fused(preset, shape):
+    """tqkv_store_verify writes the same cache bytes as tqkv_store and returns
+    the oracle's attention over the updated cache."""
+    lens, ns = shape["lens"], shape["ns"]
+    cfg = _small(preset, **{k: v for k, v in shape.items() if k not in ("lens", "ns")})
+    inp = synth.make_inputs(cfg)
+    inp["seq_lens"] = np.array(lens, np.int32)
+    N, B, Hk, S = cfg["N"], cfg["B"], cfg["Hk"], cfg["S"]
+    print("store_verify", PNAME[preset], shape, flush=True)
+    # oracle: every token below seq_lens stored, then verify
+    si, po = _token_lists_ragged(lens)
+    ref_cache = np.zeros(oracle.cache_bytes(preset, B, Hk, S), np.uint8)
+    oracle.store(preset, ref_cache, B, Hk, S, _rows_at(inp["K"], si, po), _rows_at(inp["V"], si, po), si, po)
+    ref = oracle.verify(preset, ref_cache, B, Hk, S, inp["Q"], inp["seq_lens"], cfg["Hq"], True)
+    # GPU: the cached part with tqkv_store, the N new tokens with the fused call
+    cache = tq.Cache(preset, B, Hk, S)
+    si0, po0 = _token_lists_ragged([L - N for L in lens])
+    if len(si0):
+        tq.tqkv_store(cache, to_dev(_rows_at(inp["K"], si0, po0)), to_dev(_rows_at(inp["V"], si0, po0)),
+                      to_dev(si0), to_dev(po0))
+    Kn = np.stack([inp["K"][np.arange(B), np.array(lens) - N + n] for n in range(N)])  # [N, B, Hk, 128]
+    Vn = np.stack([inp["V"][np.arange(B), np.array(lens) - N + n] for n in range(N)])
+    out = tq.tqkv_store_verify(cache, to_dev(Kn), to_dev(Vn), to_dev(inp["Q"]), to_dev(inp["seq_lens"]),
+                               N, cfg["Hq"], True, num_splits=ns)
+    torch.cuda.synchronize()
+    got_cache = cache.buffer.cpu().numpy()
+    assert np.array_equal(got_cache, ref_cache), "%d bytes differ" % int((got_cache != ref_cache).sum())
+    assert_close(out.cpu().numpy(), ref, what="fused " + str(shape))
