@@ -55,12 +55,53 @@ __device__ inline int lloyd_code(float y)
     return c;
 }
 
+// x from lane (lane ^ S) of the wavefront, S = 1, 2, ..., 32, without the
+// LDS crossbar: DPP moves within rows of 16 lanes (xor 1, 2: quad
+// permutations; xor 4: half-row mirror then quad reversal; xor 8: row
+// rotation by 8) and lane-swap instructions across rows (xor 16, 32).
+template <int S> __device__ inline uint32_t lane_xor(uint32_t x, int lane)
+{
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "xor distance");
+    if constexpr (S == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false); // quad_perm [1,0,3,2]
+    } else if constexpr (S == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false); // quad_perm [2,3,0,1]
+    } else if constexpr (S == 4) {
+        const int m = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false); // row_half_mirror: i -> 7 - i
+        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);     // quad_perm [3,2,1,0]
+    } else if constexpr (S == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false); // row_ror:8
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+template <int S> __device__ inline float lane_xor(float x, int lane)
+{
+    return __uint_as_float(lane_xor<S>(__float_as_uint(x), lane));
+}
+// runtime distance (unrolled loops pass compile-time values; the switch folds)
+template <typename T> __device__ inline T lane_xor_n(T x, int s, int lane)
+{
+    switch (s) {
+    case 1: return lane_xor<1>(x, lane);
+    case 2: return lane_xor<2>(x, lane);
+    case 4: return lane_xor<4>(x, lane);
+    case 8: return lane_xor<8>(x, lane);
+    case 16: return lane_xor<16>(x, lane);
+    default: return lane_xor<32>(x, lane);
+    }
+}
+
 // Sum over the wavefront of one value per lane by xor-butterflies 32..1.
-__device__ inline float wave_tree_sum(float a)
+__device__ inline float wave_tree_sum(float a, int lane)
 {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1)
-        a = __fadd_rn(a, __shfl_xor(a, s, 64));
+        a = __fadd_rn(a, lane_xor_n(a, s, lane));
     return a;
 }
 
@@ -114,10 +155,10 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
     // ---------------------------------------------------------------- keys
     float x0 = h2f_q(in.k0), x1 = h2f_q(in.k1);
     if constexpr (PRESET == kPresetK3V4) {
-        const float n = sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(x0, x0), __fmul_rn(x1, x1))));
+        const float n = sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(x0, x0), __fmul_rn(x1, x1)), lane));
 #pragma unroll
         for (int h = 1; h < 64; h <<= 1) {
-            float p0 = __shfl_xor(x0, h, 64), p1 = __shfl_xor(x1, h, 64);
+            float p0 = lane_xor_n(x0, h, lane), p1 = lane_xor_n(x1, h, lane);
             if (lane & h) {
                 x0 = __fsub_rn(p0, x0);
                 x1 = __fsub_rn(p1, x1);
@@ -135,7 +176,7 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
         const int c0 = lloyd_code(__fmul_rn(x0, r));
         const int c1 = lloyd_code(__fmul_rn(x1, r));
         const float q0 = centroid(c0), q1 = centroid(c1);
-        const float gam = __fdiv_rn(1.0f, sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(q0, q0), __fmul_rn(q1, q1)))));
+        const float gam = __fdiv_rn(1.0f, sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(q0, q0), __fmul_rn(q1, q1)), lane)));
 
         // Bit placement: coordinate d = 64h + 32g + 8k + e -> dword triple
         // 6h+3g+{0,1,2}, byte lane e%4, slot 2k + e/4.  Slots 0-5 hold all
@@ -164,7 +205,7 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int j = 0; j < 3; ++j)
-                    w[hh][j] |= __shfl_xor(w[hh][j], s, 64);
+                    w[hh][j] |= lane_xor_n(w[hh][j], s, lane);
         if ((lane & 31) == 0) {
             const int g = lane >> 5;
             uint32_t *kd = reinterpret_cast<uint32_t *>(blk + tb * L::kKeyBytesPerToken);
@@ -182,7 +223,7 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
         float amax = fmaxf(fmaxf(0.0f, fabsf(x0)), fabsf(x1));
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+            amax = fmaxf(amax, lane_xor_n(amax, s, lane));
         const uint16_t sh = f2h(__fdiv_rn(amax, 448.0f));
         const float s = h2f_q(sh);
         const uint32_t c0 = (s == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x0, s));
@@ -200,8 +241,8 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
     float mx = fmaxf(fmaxf(__int_as_float(0xFF800000), v0), v1);
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, s, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+        mn = fminf(mn, lane_xor_n(mn, s, lane));
+        mx = fmaxf(mx, lane_xor_n(mx, s, lane));
     }
     const uint16_t zh = f2h(__fadd_rn(mn, 0.0f)); // -0 -> +0
     const float zero = h2f_q(zh);
@@ -214,7 +255,7 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
         return (q > 0.0f) ? ((q >= 15.0f) ? 15u : (uint32_t)q) : 0u;
     };
     const uint32_t vc0 = vcode(v0), vc1 = vcode(v1);
-    const uint32_t o0 = __shfl_xor(vc0, 1, 64), o1 = __shfl_xor(vc1, 1, 64);
+    const uint32_t o0 = lane_xor<1>(vc0, lane), o1 = lane_xor<1>(vc1, lane);
     // even lane: byte l/2 = (d=l | d=l+1); odd lane: byte 32 + l/2 = (d=l+63 | d=l+64)
     const int pbyte = (lane & 1) ? (32 + (lane >> 1)) : (lane >> 1);
     const uint32_t byte = (lane & 1) ? (o1 | (vc1 << 4)) : (vc0 | (o0 << 4));
