@@ -39,6 +39,16 @@
  * key scale, value scale, value zero).  The exact byte and bit placement is
  * specified in the design notes of this repository; the stored bytes of a
  * token depend only on that token's K and V.
+ *
+ * Paged cache (tqkv_paged_cache).  The cache the pages measure is a pool of
+ * blocks of 16 tokens, each holding those tokens for every KV head ("Roofline"
+ * of Part 2: blocks x 16 tokens x Hk x slot bytes).  Here a page is exactly
+ * that: page p of the pool holds Hk of the 16-token blocks above, head hk's
+ * block at base + (p * Hk + hk) * tqkv_block_bytes(preset), byte-identical to
+ * the block a contiguous cache holds for the same 16 tokens.  A block table
+ * maps the 16-token run j of sequence b (tokens [16 j, 16 j + 16)) to its
+ * page, in the manner of a paged serving engine; the store addresses tokens
+ * by slot = page * 16 + position in the page.
  */
 #ifndef TQKV_H
 #define TQKV_H
@@ -52,7 +62,9 @@ extern "C" {
 
 #define TQKV_HEAD_DIM 128    /* the only supported head size */
 #define TQKV_BLOCK_TOKENS 16 /* tokens per cache block */
-#define TQKV_MAX_ROWS 64     /* (Hq / Hk) * n_spec must not exceed this */
+#define TQKV_MAX_QLEN 128    /* queries per sequence (n_spec, or the largest ragged count) */
+#define TQKV_MAX_ROWS 8192   /* (Hq / Hk) * queries per sequence must not exceed this */
+#define TQKV_MAX_PAGES_PER_SEQ 524288 /* block-table row length of a paged cache (8M tokens) */
 
 typedef enum {
     TQKV_K8V4 = 1,    /* FP8 E4M3 keys with a per-token fp16 scale, 4-bit values */
@@ -85,6 +97,24 @@ typedef struct tqkv_cache {
     void *base;      /* device pointer */
 } tqkv_cache;
 
+/* A paged quantised KV cache: a pool of num_pages pages in caller-owned
+ * device memory of tqkv_paged_cache_bytes(preset, Hk, D, num_pages) bytes,
+ * 16-byte aligned, and (for the verify calls) the block table of a batch of
+ * B sequences.  The stores need only the pool fields. */
+typedef struct tqkv_paged_cache {
+    int32_t preset;             /* tqkv_preset */
+    int32_t Hk;                 /* KV heads */
+    int32_t D;                  /* head size, must be 128 */
+    int32_t num_pages;          /* pages in the pool, at most 2^27 - 1 */
+    void *base;                 /* device pointer to the pool */
+    const int32_t *block_table; /* device int32 [B, max_pages], 4-byte aligned: page of
+                                   tokens [16 j, 16 j + 16) of sequence b at
+                                   block_table[b * max_pages + j] */
+    int32_t B;                  /* sequences of the batch */
+    int32_t max_pages;          /* row length of the block table: token capacity
+                                   16 * max_pages per sequence, <= TQKV_MAX_PAGES_PER_SEQ */
+} tqkv_paged_cache;
+
 /* Bytes per token and KV head: 120 (k3v4_nc) or 198 (k8v4); 0 for a bad preset. */
 size_t tqkv_slot_bytes(int preset);
 
@@ -93,6 +123,10 @@ size_t tqkv_block_bytes(int preset);
 
 /* Bytes of a whole cache; 0 for invalid arguments. */
 size_t tqkv_cache_bytes(int preset, int B, int Hk, int D, int max_seq);
+
+/* Bytes of a paged pool of num_pages pages: num_pages * Hk * tqkv_block_bytes(preset);
+ * 0 for invalid arguments. */
+size_t tqkv_paged_cache_bytes(int preset, int Hk, int D, int num_pages);
 
 /* store(K, V, codes): quantise T new tokens for all Hk heads into the cache.
  *   K, V     device, fp16 [T, Hk, 128] (row-major), 2-byte aligned
@@ -111,6 +145,16 @@ size_t tqkv_cache_bytes(int preset, int B, int Hk, int D, int max_seq);
 int tqkv_store(const tqkv_cache *cache, const void *K, const void *V, const int32_t *seq_idx,
                const int32_t *pos, int T, void *stream);
 
+/* tqkv_store into a paged pool (block_table, B and max_pages are not used):
+ *   slot_mapping  device, int32 [T], 4-byte aligned: token t goes to
+ *                 position slot % 16 of page slot / 16; a negative slot
+ *                 (padding) or a page >= num_pages is skipped
+ * The bytes written for a token are those tqkv_store writes for it.  Slots
+ * must be distinct within one call.  T == 0 is a no-op.
+ * Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_paged_store(const tqkv_paged_cache *cache, const void *K, const void *V, const int32_t *slot_mapping,
+                     int T, void *stream);
+
 /* Number of key-range partitions tqkv_verify uses for num_splits (0 = auto)
  * on this cache and shape; 0 for invalid arguments. */
 int tqkv_verify_num_splits(const tqkv_cache *cache, int n_spec, int Hq, int num_splits);
@@ -123,7 +167,8 @@ int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int
 
 /* verify(Q, cache, lens): attention of n_spec speculative queries per
  * sequence over the quantised cache.
- *   Q         device, [n_spec, B, Hq, 128] of q_dtype, 16-byte aligned
+ *   Q         device, [n_spec, B, Hq, 128] of q_dtype, 16-byte aligned;
+ *             1 <= n_spec <= TQKV_MAX_QLEN, (Hq / Hk) * n_spec <= TQKV_MAX_ROWS
  *   seq_lens  device, int32 [B]: tokens in the cache for sequence b, the
  *             n_spec speculative ones included (cached_len = seq_lens[b] - n_spec)
  *   causal    1: query n attends to tokens [0, cached_len + n + 1);
@@ -145,6 +190,24 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
                 int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* tqkv_verify with a different number of queries per sequence, packed (the
+ * verify of per-sequence draft lengths, or a continuation chunk of up to
+ * TQKV_MAX_QLEN tokens; the integration path of the pages' Part 6):
+ *   cu_q      device, int32 [B + 1], 4-byte aligned: sequence b owns query
+ *             rows [cu_q[b], cu_q[b + 1]) of Q and out, q_b = their count;
+ *             its queries are its last q_b tokens (cached_len = seq_lens[b] - q_b)
+ *   max_q     host: an upper bound of every q_b, 1 <= max_q <= TQKV_MAX_QLEN;
+ *             counts above it are cut to max_q; the workspace and split
+ *             count are those of tqkv_verify with n_spec = max_q
+ *   Q         device, [cu_q[B], Hq, 128] of q_dtype, 16-byte aligned
+ *   out       device, fp32 [cu_q[B], Hq, 128], 16-byte aligned
+ * Query n of sequence b attends to tokens [0, cached_len + n + 1) (causal)
+ * or [0, seq_lens[b]).  Rows of out that no sequence owns are not written.
+ * Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_verify_varlen(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *cu_q, int max_q,
+                       const int32_t *seq_lens, int Hq, int causal, int num_splits, float sm_scale, float *out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* store + verify in one launch, for the speculative-decode step of the
  * pages' Part 4 (the N_spec draft tokens are written to the cache, then
  * their queries attend to it):
@@ -153,13 +216,36 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
  *             (exactly the bytes tqkv_store writes for it)
  *   the other arguments and the result are those of tqkv_verify.
  * Equivalent to tqkv_store of those n_spec * B tokens followed by
- * tqkv_verify, without the separate store launch; the work-groups that read
- * the new tokens' tiles quantise them first.  Same preconditions as
- * tqkv_verify, plus n_spec <= seq_lens[b].
+ * tqkv_verify; for small steps (n_spec * ceil(Hq / Hk * n_spec / 32) <= 32)
+ * without the separate store launch: the work-groups that read the new
+ * tokens' tiles quantise them first.  Same preconditions as tqkv_verify,
+ * plus n_spec <= seq_lens[b].
  * Returns TQKV_OK or a negative tqkv_status. */
 int tqkv_store_verify(const tqkv_cache *cache, const void *K, const void *V, const void *Q, int q_dtype,
                       const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
                       float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The verify calls on a paged cache: the same arguments, results and
+ * preconditions as tqkv_verify_num_splits, tqkv_verify_workspace_bytes,
+ * tqkv_verify, tqkv_verify_varlen and tqkv_store_verify, with every block of
+ * sequence b read from (and, for the store, written to) the page the block
+ * table names.  Besides, every table entry for tokens below seq_lens[b] must
+ * name a page of the pool holding those tokens; an entry outside
+ * [0, num_pages) reads page 0 instead (and the fused store skips it), so no
+ * access leaves the pool.  The split count is raised where needed so that
+ * one work-group covers at most 8192 tokens. */
+int tqkv_paged_verify_num_splits(const tqkv_paged_cache *cache, int n_spec, int Hq, int num_splits);
+int tqkv_paged_verify_workspace_bytes(const tqkv_paged_cache *cache, int n_spec, int Hq, int num_splits,
+                                      size_t *bytes);
+int tqkv_paged_verify(const tqkv_paged_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens,
+                      int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+int tqkv_paged_verify_varlen(const tqkv_paged_cache *cache, const void *Q, int q_dtype, const int32_t *cu_q,
+                             int max_q, const int32_t *seq_lens, int Hq, int causal, int num_splits, float sm_scale,
+                             float *out, void *workspace, size_t workspace_bytes, void *stream);
+int tqkv_paged_store_verify(const tqkv_paged_cache *cache, const void *K, const void *V, const void *Q, int q_dtype,
+                            const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
+                            float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *tqkv_status_string(int status);

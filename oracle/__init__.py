@@ -42,6 +42,10 @@ PINS = {
     "quant_val": "|v - vhat| <= scale/2; endpoints hit codes 0 and 15; constant vector exact",
     "record layout": "parity unpinned (a layout choice): round trip pack/unpack and worked bytes only",
     "verify": "torch SDPA in float64 on materialised K/V; brute-force special cases; causality",
+    "store_paged / gather_pages": "a paged store gathered through its block table equals the contiguous "
+                                  "store byte for byte (layout: parity unpinned, as above)",
+    "verify_varlen": "equal query counts reduce to verify; each sequence equals a one-sequence verify "
+                     "with its own count; SDPA on materialised K/V with the per-row causal window",
 }
 
 
@@ -93,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.tqo_read_record.argtypes = [i32, P, i32, P, P, P, P, P, P]
         L.tqo_store.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i32]
         L.tqo_store.restype = i32
+        L.tqo_store_paged.argtypes = [i32, i32, i32, P, P, P, P, i32]
+        L.tqo_store_paged.restype = i32
         L.tqo_dequant.argtypes = [i32, i32, i32, P, i32, i32, i32, P, P, P]
         L.tqo_verify.argtypes = [i32, i32, i32, i32, P, P, i32, P, i32, i32, i32,
                                  ctypes.c_double, P]
@@ -265,4 +271,67 @@ def verify(preset: int, cache: np.ndarray, B: int, Hk: int, max_seq: int, Q: np.
                           int(bool(causal)), float(sm_scale), _p(out))
     if rc != 0:
         raise ValueError("oracle verify: bad arguments")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# paged pool and ragged queries
+# ----------------------------------------------------------------------------
+
+def paged_cache_bytes(preset: int, Hk: int, num_pages: int) -> int:
+    """A pool of num_pages pages, each the 16-token blocks of all Hk heads."""
+    return num_pages * Hk * block_bytes(preset)
+
+
+def store_paged(preset: int, pool: np.ndarray, Hk: int, num_pages: int, K: np.ndarray, V: np.ndarray,
+                slots: np.ndarray) -> None:
+    """Quantise K, V (float16 [T, Hk, 128]) into the paged ``pool`` (uint8, in
+    place) at slots[t] = page * 16 + position; negative slots are skipped."""
+    assert pool.dtype == np.uint8 and pool.size == paged_cache_bytes(preset, Hk, num_pages)
+    Kh = np.ascontiguousarray(K, np.float16).view(np.uint16)
+    Vh = np.ascontiguousarray(V, np.float16).view(np.uint16)
+    T = Kh.shape[0]
+    assert Kh.shape == (T, Hk, D) and Vh.shape == (T, Hk, D)
+    sl = np.ascontiguousarray(slots, np.int32)
+    assert sl.shape == (T,)
+    rc = lib().tqo_store_paged(preset, Hk, num_pages, _p(pool), _p(Kh), _p(Vh), _p(sl), T)
+    if rc != 0:
+        raise ValueError("oracle paged store: page out of range")
+
+
+def gather_pages(preset: int, pool: np.ndarray, Hk: int, num_pages: int, block_table: np.ndarray) -> np.ndarray:
+    """The contiguous cache (B sequences, max_seq = 16 * max_pages) whose block
+    j of (b, hk) is head hk's block of page block_table[b, j]; entries outside
+    the pool give zero blocks.  Pure byte movement: no arithmetic."""
+    bb = block_bytes(preset)
+    B, P = block_table.shape
+    blocks = pool.reshape(num_pages, Hk, bb)
+    out = np.zeros((B, Hk, P, bb), np.uint8)
+    for b in range(B):
+        for j in range(P):
+            pg = int(block_table[b, j])
+            if 0 <= pg < num_pages:
+                out[b, :, j, :] = blocks[pg]
+    return out.reshape(-1)
+
+
+def verify_varlen(preset: int, cache: np.ndarray, B: int, Hk: int, max_seq: int, Q: np.ndarray,
+                  cu_q: np.ndarray, seq_lens: np.ndarray, Hq: int, causal: bool,
+                  sm_scale: float = 0.0) -> np.ndarray:
+    """float64 [rows, Hq, 128]: sequence b's q_b = cu_q[b+1] - cu_q[b] queries
+    (rows cu_q[b].. of Q [rows, Hq, 128]) are its last q_b tokens, attended
+    exactly as ``verify`` attends a step of q_b queries of that sequence alone
+    ("Speculative decoding on Intel Arc", Part 6: each continuation chunk of
+    up to 128 queries is a decode over its own cached length)."""
+    rows = Q.shape[0]
+    assert Q.shape == (rows, Hq, D) and cu_q.shape == (B + 1,)
+    out = np.full((rows, Hq, D), np.nan, np.float64)
+    per_seq = cache_bytes(preset, 1, Hk, max_seq)
+    for b in range(B):
+        c0, c1 = int(cu_q[b]), int(cu_q[b + 1])
+        if c1 <= c0:
+            continue
+        cb = cache[b * per_seq:(b + 1) * per_seq]
+        out[c0:c1] = verify(preset, cb, 1, Hk, max_seq, Q[c0:c1][:, None], np.asarray(seq_lens[b:b + 1]),
+                            Hq, causal, sm_scale)[:, 0]
     return out

@@ -522,6 +522,48 @@ int tqo_store(int preset, int B, int Hk, int max_seq, uint8_t *cache, const uint
 }
 
 /* ------------------------------------------------------------------------ */
+/* store into a paged pool: page p holds the 16-token blocks of every KV     */
+/* head, head hk's at pool + (p * Hk + hk) * block bytes (the pages' cache   */
+/* is counted as blocks of 16 tokens x Hk heads: "Speculative decoding on    */
+/* Intel Arc", Part 2, Roofline).  Token t goes to slot slots[t] =            */
+/* page * 16 + position in the page; a negative slot is padding (skipped).   */
+/* Returns 0, or -1 when a page is outside the pool (nothing written for it).*/
+/* ------------------------------------------------------------------------ */
+
+int tqo_store_paged(int preset, int Hk, int num_pages, uint8_t *pool, const uint16_t *K,
+                    const uint16_t *V, const int32_t *slots, int T)
+{
+    float cb[8], th[7];
+    if (preset == TQO_K3V4_NC)
+        tqo_codebook(cb, th);
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (long th_i = 0; th_i < (long)T * Hk; ++th_i) {
+        int t = (int)(th_i / Hk), hk = (int)(th_i % Hk);
+        int sl = slots[t];
+        if (sl < 0)
+            continue;
+        int page = sl / TQO_BLOCK, tb = sl % TQO_BLOCK;
+        if (page >= num_pages) {
+            bad = 1;
+            continue;
+        }
+        const uint16_t *kh = K + ((size_t)t * Hk + hk) * TQO_D;
+        const uint16_t *vh = V + ((size_t)t * Hk + hk) * TQO_D;
+        uint8_t kc[TQO_D], vc[TQO_D];
+        uint16_t m0 = 0, m1 = 0, vs, vz;
+        if (preset == TQO_K3V4_NC)
+            tqo_quant_key_k3(kh, cb, th, kc, &m0, &m1);
+        else
+            tqo_quant_key_k8(kh, kc, &m0);
+        tqo_quant_val(vh, vc, &vs, &vz);
+        uint8_t *blk = pool + ((size_t)page * (size_t)Hk + (size_t)hk) * tqo_block_bytes(preset);
+        tqo_write_record(preset, blk, tb, kc, vc, m0, m1, vs, vz);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantisation of one token-head (binary64).                              */
 /*   k3v4_nc: khat_rot[d] = c[code] * n_h * gamma_h  (rotated space)         */
 /*   k8v4:    khat[d]     = e4m3(code) * kscale_h                            */

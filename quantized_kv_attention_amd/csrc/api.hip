@@ -33,7 +33,28 @@ int current_device_cus()
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int check_cache(const tqkv_cache *c)
+// A cache as the kernels see it: contiguous (btab null: block j of unit
+// b * Hk + hk at base + (unit * nblk + j) * block bytes) or paged (block j of
+// sequence b in page btab[b * bstride + j] of the pool).
+struct View {
+    int preset, B, Hk, max_seq; // max_seq: token capacity per sequence
+    void *base;
+    const int32_t *btab;
+    int bstride, npages;
+};
+
+int nblocks(int max_seq) { return (max_seq + kBlockTokens - 1) / kBlockTokens; }
+
+int check_preset(int preset, int D)
+{
+    if (preset != TQKV_K8V4 && preset != TQKV_K3V4_NC)
+        return TQKV_ERR_ARG;
+    if (D != TQKV_HEAD_DIM)
+        return TQKV_ERR_UNSUPPORTED;
+    return TQKV_OK;
+}
+
+int view_of(const tqkv_cache *c, View &v)
 {
     if (!c)
         return TQKV_ERR_ARG;
@@ -45,21 +66,56 @@ int check_cache(const tqkv_cache *c)
         return TQKV_ERR_UNSUPPORTED;
     if (!aligned(c->base, 16))
         return TQKV_ERR_ALIGN;
+    v = View{c->preset, c->B, c->Hk, c->max_seq, c->base, nullptr, 0, 0};
     return TQKV_OK;
 }
 
-int nblocks(int max_seq) { return (max_seq + kBlockTokens - 1) / kBlockTokens; }
+// the pool part of a paged cache (what the store needs)
+int check_pool(const tqkv_paged_cache *c)
+{
+    if (!c)
+        return TQKV_ERR_ARG;
+    if (c->preset != TQKV_K8V4 && c->preset != TQKV_K3V4_NC)
+        return TQKV_ERR_ARG;
+    if (c->Hk < 1 || c->num_pages < 1 || c->num_pages > (INT32_MAX >> 4) || !c->base)
+        return TQKV_ERR_ARG;
+    if (c->D != TQKV_HEAD_DIM)
+        return TQKV_ERR_UNSUPPORTED;
+    if (!aligned(c->base, 16))
+        return TQKV_ERR_ALIGN;
+    return TQKV_OK;
+}
+
+int view_of(const tqkv_paged_cache *c, View &v)
+{
+    int st = check_pool(c);
+    if (st != TQKV_OK)
+        return st;
+    if (!c->block_table || c->B < 1 || c->max_pages < 1)
+        return TQKV_ERR_ARG;
+    if (c->max_pages > TQKV_MAX_PAGES_PER_SEQ)
+        return TQKV_ERR_UNSUPPORTED;
+    if (!aligned(c->block_table, 4))
+        return TQKV_ERR_ALIGN;
+    v = View{c->preset, c->B, c->Hk, c->max_pages * kBlockTokens, c->base, c->block_table, c->max_pages,
+             c->num_pages};
+    return TQKV_OK;
+}
 
 // Query rows per work-group: the rows of one KV head are cut into tiles of
 // 32 (one MFMA operand height), one work-group each.
 int row_tiles(int rows) { return (rows + 31) / 32; }
 
+// A wavefront of a paged verify holds the page ids of at most 64 tiles (two
+// VGPRs), so a work-group covers at most 256 tiles of 32 tokens.
+constexpr int kPagedTilesPerGroup = 256;
+
 // Key-range partitions per (b, hk): two work-groups of 4 wavefronts per
 // compute unit overall, at least one 32-token tile per wavefront.
-int plan_splits(const tqkv_cache *c, int num_splits, int cus, int rows)
+int plan_splits(const View &c, int num_splits, int cus, int rows)
 {
-    const int units = c->B * c->Hk * row_tiles(rows);
-    const int tiles = (c->max_seq + 31) / 32;
+    const int units = c.B * c.Hk * row_tiles(rows);
+    const int tiles = (c.max_seq + 31) / 32;
     const int max_useful = (tiles + 3) / 4;
     int s = num_splits;
     if (s <= 0)
@@ -70,42 +126,73 @@ int plan_splits(const tqkv_cache *c, int num_splits, int cus, int rows)
         s = 1024;
     if (s < 1)
         s = 1;
+    if (c.btab) {
+        const int need = (tiles + kPagedTilesPerGroup - 1) / kPagedTilesPerGroup;
+        if (s < need)
+            s = need; // <= 1024 by the page limit per sequence
+    }
     return s;
 }
 
-int check_verify_shape(const tqkv_cache *c, int n_spec, int Hq)
+int check_verify_shape(const View &c, int n_spec, int Hq)
 {
-    int st = check_cache(c);
-    if (st != TQKV_OK)
-        return st;
     if (n_spec < 1 || Hq < 1)
         return TQKV_ERR_ARG;
-    if (Hq % c->Hk != 0)
+    if (Hq % c.Hk != 0)
         return TQKV_ERR_UNSUPPORTED;
-    if ((Hq / c->Hk) * n_spec > TQKV_MAX_ROWS)
+    if (n_spec > TQKV_MAX_QLEN || (long)(Hq / c.Hk) * n_spec > TQKV_MAX_ROWS)
         return TQKV_ERR_UNSUPPORTED;
     return TQKV_OK;
 }
 
 // Workspace: with more than one key range, the partial softmax states of
 // every key range (32 rows per row tile); nothing otherwise.
-size_t workspace_for(const tqkv_cache *c, int n_spec, int Hq, int splits)
+size_t workspace_for(const View &c, int n_spec, int Hq, int splits)
 {
     if (splits <= 1)
         return 0;
-    const size_t groups = (size_t)c->B * c->Hk * row_tiles((Hq / c->Hk) * n_spec);
+    const size_t groups = (size_t)c.B * c.Hk * row_tiles((Hq / c.Hk) * n_spec);
     const size_t slots = groups * splits * 32;
     return slots * 2 * sizeof(float) + slots * TQKV_HEAD_DIM * sizeof(uint16_t);
 }
 
-} // namespace
-
-namespace {
-int verify_impl(const tqkv_cache *cache, const void *Knew, const void *Vnew, const void *Q, int q_dtype,
-                       const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
-                       float *out, void *workspace, size_t workspace_bytes, void *stream)
+int num_splits_impl(const View &v, int n_spec, int Hq, int num_splits)
 {
-    int st = check_verify_shape(cache, n_spec, Hq);
+    if (check_verify_shape(v, n_spec, Hq) != TQKV_OK || num_splits < 0)
+        return 0;
+    int cus = current_device_cus();
+    if (cus < 0)
+        return 0;
+    return plan_splits(v, num_splits, cus, (Hq / v.Hk) * n_spec);
+}
+
+int workspace_impl(const View &v, int n_spec, int Hq, int num_splits, size_t *bytes)
+{
+    int st = check_verify_shape(v, n_spec, Hq);
+    if (st != TQKV_OK)
+        return st;
+    if (num_splits < 0)
+        return TQKV_ERR_ARG;
+    int cus = current_device_cus();
+    if (cus < 0)
+        return cus;
+    *bytes = workspace_for(v, n_spec, Hq, plan_splits(v, num_splits, cus, (Hq / v.Hk) * n_spec));
+    return TQKV_OK;
+}
+
+// The new tokens of a fused store + verify are quantised inside the verify
+// launch when few work-groups share them (each row tile's work-groups store
+// them again); otherwise the store kernel runs first, on the same stream.
+bool fuse_store(int n_spec, int rows) { return n_spec * row_tiles(rows) <= 32; }
+
+// store + verify (Knew, Vnew non-null) or verify; dense queries
+// [n_spec, B, Hq, 128] (cu_q null) or ragged ones (cu_q [B + 1], n_spec =
+// the largest query count)
+int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q, int q_dtype,
+                const int32_t *cu_q, const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits,
+                float sm_scale, float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = check_verify_shape(v, n_spec, Hq);
     if (st != TQKV_OK)
         return st;
     if (!Q || !seq_lens || !out || num_splits < 0)
@@ -120,38 +207,64 @@ int verify_impl(const tqkv_cache *cache, const void *Knew, const void *Vnew, con
         return TQKV_ERR_ARG;
     if (!(sm_scale >= 0.0f) || isinf(sm_scale))
         return TQKV_ERR_ARG;
-    if (!aligned(Q, 16) || !aligned(seq_lens, 4) || !aligned(out, 16))
+    if (!aligned(Q, 16) || !aligned(seq_lens, 4) || !aligned(out, 16) || !aligned(cu_q, 4))
         return TQKV_ERR_ALIGN;
     int cus = current_device_cus();
     if (cus < 0)
         return cus;
-    const int splits = plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec);
-    const size_t need = workspace_for(cache, n_spec, Hq, splits);
+    const int G = Hq / v.Hk;
+    const int R = G * n_spec;
+    const int splits = plan_splits(v, num_splits, cus, R);
+    const size_t need = workspace_for(v, n_spec, Hq, splits);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return TQKV_ERR_WORKSPACE;
         if (!aligned(workspace, 256))
             return TQKV_ERR_ALIGN;
     }
-    const int G = Hq / cache->Hk;
-    const int R = G * n_spec;
     const float scale = (sm_scale == 0.0f) ? 0.08838834764831845f : sm_scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool fused = Knew && fuse_store(n_spec, R);
+    if (Knew && !fused) {
+        // the store kernel over the n_spec new tokens of every sequence:
+        // token n of sequence b is row (n * B + b) of K and V, at position
+        // seq_lens[b] - n_spec + n (computed on the device)
+        StoreArgs sa;
+        sa.base = static_cast<uint8_t *>(v.base);
+        sa.K = static_cast<const uint16_t *>(Knew);
+        sa.V = static_cast<const uint16_t *>(Vnew);
+        sa.seq_idx = nullptr;
+        sa.pos = nullptr;
+        sa.slots = nullptr;
+        sa.step_lens = seq_lens;
+        sa.btab = v.btab;
+        sa.B = v.B;
+        sa.Hk = v.Hk;
+        sa.max_seq = v.max_seq;
+        sa.nblk = nblocks(v.max_seq);
+        sa.T = n_spec * v.B;
+        sa.N = n_spec;
+        sa.bstride = v.bstride;
+        sa.npages = v.npages;
+        if (launch_store(v.preset, sa, s) != hipSuccess)
+            return TQKV_ERR_LAUNCH;
+    }
     VerifyArgs a;
-    a.base = static_cast<const uint8_t *>(cache->base);
+    a.base = static_cast<const uint8_t *>(v.base);
     a.Q = Q;
     a.seq_lens = seq_lens;
     a.out = out;
-    const size_t groups = (size_t)cache->B * cache->Hk * row_tiles(R);
+    const size_t groups = (size_t)v.B * v.Hk * row_tiles(R);
     // workspace: (max, sum) pairs first (8-byte aligned), then the binary16 outputs
     const size_t slots = groups * splits * 32;
     a.part_ml = splits > 1 ? static_cast<float2 *>(workspace) : nullptr;
     a.part_o = splits > 1 ? reinterpret_cast<_Float16 *>(static_cast<uint8_t *>(workspace) + slots * sizeof(float2)) : nullptr;
     a.qscale = scale * 1.4426950408889634f;
     a.q_f16 = (q_dtype == TQKV_Q_F16);
-    a.Hk = cache->Hk;
-    a.max_seq = cache->max_seq;
-    a.nblk = nblocks(cache->max_seq);
-    a.B = cache->B;
+    a.Hk = v.Hk;
+    a.max_seq = v.max_seq;
+    a.nblk = nblocks(v.max_seq);
+    a.B = v.B;
     a.N = n_spec;
     a.Hq = Hq;
     a.G = G;
@@ -159,11 +272,53 @@ int verify_impl(const tqkv_cache *cache, const void *Knew, const void *Vnew, con
     a.causal = causal;
     a.nsplit = splits;
     a.nrt = row_tiles(R);
-    a.Knew = static_cast<const uint16_t *>(Knew);
-    a.Vnew = static_cast<const uint16_t *>(Vnew);
-    a.wbase = static_cast<uint8_t *>(cache->base);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_verify(cache->preset, 1, a, s) != hipSuccess)
+    a.Knew = fused ? static_cast<const uint16_t *>(Knew) : nullptr;
+    a.Vnew = fused ? static_cast<const uint16_t *>(Vnew) : nullptr;
+    a.wbase = static_cast<uint8_t *>(v.base);
+    a.cu_q = cu_q;
+    a.btab = v.btab;
+    a.bstride = v.bstride;
+    a.npages = v.npages;
+    if (launch_verify(v.preset, v.btab != nullptr, a, s) != hipSuccess)
+        return TQKV_ERR_LAUNCH;
+    return TQKV_OK;
+}
+
+int store_impl(int preset, int Hk, void *base, const tqkv_cache *c, const tqkv_paged_cache *pc, const void *K,
+               const void *V, const int32_t *seq_idx, const int32_t *pos, const int32_t *slot_mapping, int T,
+               void *stream)
+{
+    if (T < 0)
+        return TQKV_ERR_ARG;
+    if (T == 0)
+        return TQKV_OK;
+    if (!K || !V || (pc ? !slot_mapping : (!seq_idx || !pos)))
+        return TQKV_ERR_ARG;
+    if (!aligned(K, 2) || !aligned(V, 2) || !aligned(seq_idx, 4) || !aligned(pos, 4) || !aligned(slot_mapping, 4))
+        return TQKV_ERR_ALIGN;
+    if ((long)T * Hk > (long)INT32_MAX * 4)
+        return TQKV_ERR_UNSUPPORTED;
+    int cus = current_device_cus();
+    if (cus < 0)
+        return cus;
+    StoreArgs a;
+    a.base = static_cast<uint8_t *>(base);
+    a.K = static_cast<const uint16_t *>(K);
+    a.V = static_cast<const uint16_t *>(V);
+    a.seq_idx = pc ? nullptr : seq_idx;
+    a.pos = pc ? nullptr : pos;
+    a.slots = pc ? slot_mapping : nullptr;
+    a.step_lens = nullptr;
+    a.btab = nullptr;
+    a.B = pc ? 0 : c->B;
+    a.Hk = Hk;
+    a.max_seq = pc ? 0 : c->max_seq;
+    a.nblk = pc ? 0 : nblocks(c->max_seq);
+    a.T = T;
+    a.N = 0;
+    a.bstride = 0;
+    a.npages = pc ? pc->num_pages : 0;
+    if (launch_store(preset, a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return TQKV_ERR_LAUNCH;
     return TQKV_OK;
 }
@@ -190,72 +345,97 @@ size_t tqkv_cache_bytes(int preset, int B, int Hk, int D, int max_seq)
     return (size_t)B * Hk * nblocks(max_seq) * tqkv_block_bytes(preset);
 }
 
+size_t tqkv_paged_cache_bytes(int preset, int Hk, int D, int num_pages)
+{
+    if (tqkv_slot_bytes(preset) == 0 || Hk < 1 || D != TQKV_HEAD_DIM || num_pages < 1 || num_pages > (INT32_MAX >> 4))
+        return 0;
+    return (size_t)num_pages * Hk * tqkv_block_bytes(preset);
+}
+
 int tqkv_store(const tqkv_cache *cache, const void *K, const void *V, const int32_t *seq_idx,
                const int32_t *pos, int T, void *stream)
 {
-    int st = check_cache(cache);
+    View v;
+    int st = view_of(cache, v);
     if (st != TQKV_OK)
         return st;
-    if (T < 0)
-        return TQKV_ERR_ARG;
-    if (T == 0)
-        return TQKV_OK;
-    if (!K || !V || !seq_idx || !pos)
-        return TQKV_ERR_ARG;
-    if (!aligned(K, 2) || !aligned(V, 2) || !aligned(seq_idx, 4) || !aligned(pos, 4))
-        return TQKV_ERR_ALIGN;
-    int cus = current_device_cus();
-    if (cus < 0)
-        return cus;
-    StoreArgs a;
-    a.base = static_cast<uint8_t *>(cache->base);
-    a.K = static_cast<const uint16_t *>(K);
-    a.V = static_cast<const uint16_t *>(V);
-    a.seq_idx = seq_idx;
-    a.pos = pos;
-    a.B = cache->B;
-    a.Hk = cache->Hk;
-    a.max_seq = cache->max_seq;
-    a.nblk = nblocks(cache->max_seq);
-    a.T = T;
-    if (launch_store(cache->preset, a, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return TQKV_ERR_LAUNCH;
-    return TQKV_OK;
+    return store_impl(v.preset, v.Hk, v.base, cache, nullptr, K, V, seq_idx, pos, nullptr, T, stream);
+}
+
+int tqkv_paged_store(const tqkv_paged_cache *cache, const void *K, const void *V, const int32_t *slot_mapping, int T,
+                     void *stream)
+{
+    int st = check_pool(cache);
+    if (st != TQKV_OK)
+        return st;
+    return store_impl(cache->preset, cache->Hk, cache->base, nullptr, cache, K, V, nullptr, nullptr, slot_mapping, T,
+                      stream);
 }
 
 int tqkv_verify_num_splits(const tqkv_cache *cache, int n_spec, int Hq, int num_splits)
 {
-    if (check_verify_shape(cache, n_spec, Hq) != TQKV_OK || num_splits < 0)
+    View v;
+    if (view_of(cache, v) != TQKV_OK)
         return 0;
-    int cus = current_device_cus();
-    if (cus < 0)
-        return 0;
-    return plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec);
+    return num_splits_impl(v, n_spec, Hq, num_splits);
 }
 
-int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int num_splits,
-                                size_t *bytes)
+int tqkv_paged_verify_num_splits(const tqkv_paged_cache *cache, int n_spec, int Hq, int num_splits)
+{
+    View v;
+    if (view_of(cache, v) != TQKV_OK)
+        return 0;
+    return num_splits_impl(v, n_spec, Hq, num_splits);
+}
+
+int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int num_splits, size_t *bytes)
 {
     if (!bytes)
         return TQKV_ERR_ARG;
     *bytes = 0;
-    int st = check_verify_shape(cache, n_spec, Hq);
+    View v;
+    int st = view_of(cache, v);
     if (st != TQKV_OK)
         return st;
-    if (num_splits < 0)
+    return workspace_impl(v, n_spec, Hq, num_splits, bytes);
+}
+
+int tqkv_paged_verify_workspace_bytes(const tqkv_paged_cache *cache, int n_spec, int Hq, int num_splits,
+                                      size_t *bytes)
+{
+    if (!bytes)
         return TQKV_ERR_ARG;
-    int cus = current_device_cus();
-    if (cus < 0)
-        return cus;
-    *bytes = workspace_for(cache, n_spec, Hq, plan_splits(cache, num_splits, cus, (Hq / cache->Hk) * n_spec));
-    return TQKV_OK;
+    *bytes = 0;
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    return workspace_impl(v, n_spec, Hq, num_splits, bytes);
 }
 
 int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens,
                 int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
                 void *workspace, size_t workspace_bytes, void *stream)
 {
-    return verify_impl(cache, nullptr, nullptr, Q, q_dtype, seq_lens, n_spec, Hq, causal, num_splits, sm_scale, out,
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    return verify_impl(v, nullptr, nullptr, Q, q_dtype, nullptr, seq_lens, n_spec, Hq, causal, num_splits, sm_scale,
+                       out, workspace, workspace_bytes, stream);
+}
+
+int tqkv_verify_varlen(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *cu_q, int max_q,
+                       const int32_t *seq_lens, int Hq, int causal, int num_splits, float sm_scale, float *out,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    if (!cu_q)
+        return TQKV_ERR_ARG;
+    return verify_impl(v, nullptr, nullptr, Q, q_dtype, cu_q, seq_lens, max_q, Hq, causal, num_splits, sm_scale, out,
                        workspace, workspace_bytes, stream);
 }
 
@@ -263,10 +443,54 @@ int tqkv_store_verify(const tqkv_cache *cache, const void *K, const void *V, con
                       const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
                       float *out, void *workspace, size_t workspace_bytes, void *stream)
 {
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
     if (!K || !V)
         return TQKV_ERR_ARG;
-    return verify_impl(cache, K, V, Q, q_dtype, seq_lens, n_spec, Hq, causal, num_splits, sm_scale, out, workspace,
-                       workspace_bytes, stream);
+    return verify_impl(v, K, V, Q, q_dtype, nullptr, seq_lens, n_spec, Hq, causal, num_splits, sm_scale, out,
+                       workspace, workspace_bytes, stream);
+}
+
+int tqkv_paged_verify(const tqkv_paged_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens,
+                      int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    return verify_impl(v, nullptr, nullptr, Q, q_dtype, nullptr, seq_lens, n_spec, Hq, causal, num_splits, sm_scale,
+                       out, workspace, workspace_bytes, stream);
+}
+
+int tqkv_paged_verify_varlen(const tqkv_paged_cache *cache, const void *Q, int q_dtype, const int32_t *cu_q,
+                             int max_q, const int32_t *seq_lens, int Hq, int causal, int num_splits, float sm_scale,
+                             float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    if (!cu_q)
+        return TQKV_ERR_ARG;
+    return verify_impl(v, nullptr, nullptr, Q, q_dtype, cu_q, seq_lens, max_q, Hq, causal, num_splits, sm_scale, out,
+                       workspace, workspace_bytes, stream);
+}
+
+int tqkv_paged_store_verify(const tqkv_paged_cache *cache, const void *K, const void *V, const void *Q, int q_dtype,
+                            const int32_t *seq_lens, int n_spec, int Hq, int causal, int num_splits, float sm_scale,
+                            float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    if (!K || !V)
+        return TQKV_ERR_ARG;
+    return verify_impl(v, K, V, Q, q_dtype, nullptr, seq_lens, n_spec, Hq, causal, num_splits, sm_scale, out,
+                       workspace, workspace_bytes, stream);
 }
 
 const char *tqkv_status_string(int status)
@@ -283,6 +507,6 @@ const char *tqkv_status_string(int status)
     }
 }
 
-int tqkv_version(void) { return 100; }
+int tqkv_version(void) { return 110; }
 
 } // extern "C"

@@ -11,7 +11,6 @@ constexpr int kD = 128;
 constexpr int kBlockTokens = 16;
 constexpr int kPresetK8V4 = 1;
 constexpr int kPresetK3V4 = 2;
-constexpr int kMaxRows = 64;
 
 // Byte layout of one 16-token block (see include/tqkv.h for the overview).
 //   k3v4_nc: key codes [0,768) 48 B/token | value nibbles [768,1792) |
@@ -50,13 +49,23 @@ __host__ __device__ inline int val_byte_offset(int tb, int p)
     return dw * 4 + pos;
 }
 
+// Where token t (row t of K and V [T, Hk, 128]) goes, in this order:
+//   step_lens non-null: a speculative step of N tokens per sequence, T = N * B;
+//     token t = n * B + b goes to position step_lens[b] - N + n of sequence b
+//     (contiguous cache, or paged through the block table btab);
+//   slots non-null: paged cache, slot = page * 16 + position in the page;
+//   otherwise: contiguous cache, sequence seq_idx[t], position pos[t].
 struct StoreArgs {
     uint8_t *base;
     const uint16_t *K;
     const uint16_t *V;
     const int32_t *seq_idx;
     const int32_t *pos;
+    const int32_t *slots;
+    const int32_t *step_lens;
+    const int32_t *btab;
     int B, Hk, max_seq, nblk, T;
+    int N, bstride, npages;
 };
 
 struct VerifyArgs {
@@ -72,6 +81,16 @@ struct VerifyArgs {
     int Hk, max_seq, nblk;
     int B, N, Hq, G, R, causal, nsplit;
     int nrt; // row tiles per (b, hk): one work-group each
+    // ragged queries (non-null): device [B + 1] prefix sums of the query
+    // counts; query n of sequence b is row cu_q[b] + n of Q [*, Hq, 128] and
+    // out, and N is the largest count.  Null: Q and out are [N, B, Hq, 128].
+    const int32_t *cu_q;
+    // paged cache (non-null): device [B, bstride] page ids; block j of
+    // sequence b, head hk is at base + (btab[b * bstride + j] * Hk + hk) *
+    // block bytes.  Null: block j of unit u = b * Hk + hk is at
+    // base + (u * nblk + j) * block bytes.
+    const int32_t *btab;
+    int bstride, npages;
     // fused store (null for a plain verify): the n_spec new tokens of every
     // sequence, fp16 [N, B, Hk, 128]; token n of sequence b goes to position
     // seq_lens[b] - N + n of the cache before it is attended to
@@ -81,6 +100,6 @@ struct VerifyArgs {
 
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
-hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_verify(int preset, bool paged, const VerifyArgs &a, hipStream_t s);
 
 } // namespace tqkv

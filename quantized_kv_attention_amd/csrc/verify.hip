@@ -167,6 +167,38 @@ __device__ inline void issue_tile(const uint8_t *ubase, int kt, int nblk, uint32
     }
 }
 
+// The same for a paged cache, where the tile's two blocks sit at unrelated
+// addresses src0 and src1 (both = false: the tile has only its first block).
+// Loads before the block boundary read src0, loads after it src1; the one
+// load that straddles the boundary (block bytes are a multiple of 16, so
+// the boundary falls between two lanes) takes a per-lane address.
+template <int PRESET>
+__device__ inline void issue_tile_paged(const uint8_t *src0, const uint8_t *src1, bool both, uint32_t slot_lds,
+                                        uint32_t voff, uint32_t voff_last, int lane)
+{
+    using L = Layout<PRESET>;
+    constexpr int LPT = Ring<PRESET>::kLoads, BB = L::kBlockBytes;
+    constexpr int JS = BB / 1024;                      // the straddling load
+    constexpr int kSplitLane = (BB - 1024 * JS) / 16; // its first lane in block 1
+    static_assert(BB % 16 == 0 && kSplitLane > 0 && JS < LPT - 1, "tile split");
+    if (__builtin_expect(both, 1)) {
+#pragma unroll
+        for (int j = 0; j < JS; ++j)
+            dma16_s(src0 + 1024 * j, voff, slot_lds + 1024 * j);
+        const uint8_t *ps = (lane < kSplitLane) ? src0 + (1024 * JS + 16 * lane)
+                                                : src1 + (16 * (lane - kSplitLane));
+        dma16(ps, slot_lds + 1024 * JS);
+#pragma unroll
+        for (int j = JS + 1; j < LPT - 1; ++j)
+            dma16_s(src1 + (1024 * j - BB), voff, slot_lds + 1024 * j);
+        dma16_s(src1 + (1024 * (LPT - 1) - BB), voff_last, slot_lds + 1024 * (LPT - 1));
+    } else {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j)
+            dma16_s(src0, (uint32_t)min(1024 * j + 16 * lane, BB - 16), slot_lds + 1024 * j);
+    }
+}
+
 // Maximum / sum of a per-lane value over the two lane halves (lanes l and
 // l ^ 32 hold the same query row): one v_permlane32_swap.
 __device__ inline void swap_halves(float x, float &a, float &b)
@@ -399,7 +431,7 @@ __device__ inline half8_t hadamard_operand(int o, int ks, int h)
     return r.h;
 }
 
-template <int PRESET, int NQT>
+template <int PRESET, int NQT, bool PAGED>
 __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArgs a)
 {
     constexpr int RP = 32 * NQT; // padded rows
@@ -436,9 +468,21 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     const int b = unit / a.Hk, hk = unit % a.Hk;
     const int Lr = a.seq_lens[b];
     const int L = Lr < 0 ? 0 : (Lr > a.max_seq ? a.max_seq : Lr);
-    // row r of the unit is query head hk * G + r % G of speculative token
-    // r / G; the quotient comes from a float reciprocal (exact: r < 64 and
-    // (r + 0.5) / G stays at least 0.5 / G away from an integer)
+    // this sequence's queries: nq of them, query n in row qt0 + n * qts of Q
+    // and out; they are the last nq tokens of the sequence
+    int nq = a.N, qt0 = b, qts = a.B;
+    if (a.cu_q) {
+        qt0 = a.cu_q[b];
+        nq = min(max(a.cu_q[b + 1] - qt0, 0), a.N);
+        qts = 1;
+    }
+    const int Rb = a.G * nq; // query rows of this unit
+    if (row0 >= Rb)
+        return; // a row tile past a short sequence's rows: nothing to do
+    // row r of the unit is query head hk * G + r % G of query r / G; the
+    // quotient comes from a float reciprocal (exact: with r < 2^20 the
+    // rounding error of (r + 0.5) * rcp(G) stays far below the distance
+    // 0.5 / G of (r + 0.5) / G to the nearest integer)
     const float rcpG = __builtin_amdgcn_rcpf((float)a.G);
     auto row_token = [&](int r) { return (int)(((float)r + 0.5f) * rcpG); };
 
@@ -452,7 +496,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     const int ntile = kt1 - kt0;
 
     using L_ = Layout<PRESET>;
-    const uint8_t *ubase = a.base + (size_t)unit * a.nblk * L_::kBlockBytes;
+    const uint8_t *ubase = a.base + (size_t)unit * a.nblk * L_::kBlockBytes; // contiguous cache
     const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t *)lds;
     const uint32_t ring_lds = lds0 + kQRegion + wave * DEPTH * kSlotBytes;
     const uint8_t *ring = lds + kQRegion + wave * DEPTH * kSlotBytes;
@@ -470,11 +514,26 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         const int rsub = lane >> rshift, cb = 16 * (lane & ((1 << rshift) - 1));
         for (int J = wave; J < RP / rpi; J += kWaves) {
             const int r = row0 + J * rpi + rsub;
-            const int rs = r < a.R ? r : 0;
+            const int rs = r < Rb ? r : 0;
             const int n = row_token(rs), g = rs - n * a.G;
             const uint8_t *src = static_cast<const uint8_t *>(a.Q) +
-                                 ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD * esz + cb;
+                                 ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD * esz + cb;
             dma16(src, lds0 + 1024 * J);
+        }
+    }
+    // paged cache: the page ids of this wavefront's blocks 2 kt0 + [0, 128)
+    // (lane l of pidv[c]: block 2 kt0 + 64 c + l; the launch plan keeps a
+    // wavefront at no more than 64 tiles).  Ids outside the pool read page
+    // 0, so no load leaves the pool whatever the table holds.
+    const int nbl = (L + kBlockTokens - 1) / kBlockTokens; // blocks holding tokens
+    const int32_t *brow = PAGED ? a.btab + (size_t)b * a.bstride : nullptr;
+    int pidv[2] = {0, 0};
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int j = 2 * kt0 + 64 * c + lane;
+            const int p = (j < nbl) ? brow[j] : 0;
+            pidv[c] = (p >= 0 && p < a.npages) ? p : 0;
         }
     }
     __builtin_amdgcn_s_barrier();
@@ -486,13 +545,42 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     const uint32_t voff = 16 * lane;
     const uint32_t voff_last = (uint32_t)min(16 * lane, 2 * L_::kBlockBytes - 16 - 1024 * (LPT - 1));
     int issued = 0; // tiles of this wavefront issued so far (wave-uniform)
+    // queue the loads of this wavefront's tile t (tile kt0 + t of the unit)
+    auto issue = [&](int t, uint32_t slot) {
+        if constexpr (!PAGED) {
+            issue_tile<PRESET>(ubase, kt0 + t, a.nblk, slot, voff, voff_last, lane);
+        } else {
+            const int j = 2 * t;
+            int p0, p1;
+            if (j < 64) {
+                p0 = __builtin_amdgcn_readlane(pidv[0], j);
+                p1 = __builtin_amdgcn_readlane(pidv[0], j + 1);
+            } else {
+                p0 = __builtin_amdgcn_readlane(pidv[1], (j - 64) & 63);
+                p1 = __builtin_amdgcn_readlane(pidv[1], (j - 63) & 63);
+            }
+            const uint8_t *src0 = a.base + ((size_t)p0 * a.Hk + hk) * L_::kBlockBytes;
+            const uint8_t *src1 = a.base + ((size_t)p1 * a.Hk + hk) * L_::kBlockBytes;
+            issue_tile_paged<PRESET>(src0, src1, 2 * (kt0 + t) + 1 < nbl, slot, voff, voff_last, lane);
+        }
+    };
+    // the cache block holding token t, for the fused store (null: a page id
+    // outside the pool, nothing is stored)
+    auto store_block = [&](int t) -> uint8_t * {
+        if constexpr (!PAGED) {
+            return a.wbase + ((size_t)unit * a.nblk + (t >> 4)) * L_::kBlockBytes;
+        } else {
+            const int p = brow[t >> 4];
+            return (p >= 0 && p < a.npages) ? a.wbase + ((size_t)p * a.Hk + hk) * L_::kBlockBytes : nullptr;
+        }
+    };
     // fused store: new tokens [tn0, L) of this unit; tiles holding them are
     // loaded only after they have been stored (step 3)
-    const int tn0 = (a.Knew != nullptr) ? L - a.N : L;
+    const int tn0 = (a.Knew != nullptr) ? L - nq : L;
     const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile); // this work-group's share
     const int pre = min(kInitTiles, max(0, min(ntile, (tn0 - kt0 * kTile) / kTile)));
     for (; issued < pre; ++issued)
-        issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + issued * kSlotBytes, voff, voff_last, lane);
+        issue(issued, ring_lds + issued * kSlotBytes);
 
     // 3. Fused store: the work-group whose key range holds new tokens of
     //    this unit quantises them into the cache first (the bytes tqkv_store
@@ -504,21 +592,24 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         // two token-heads per wavefront at a time, both loaded up front
         for (int t = wn0 + wave; t < wn1; t += 2 * kWaves) {
             const int t2 = t + kWaves;
-            const size_t src = ((size_t)((t - (L - a.N)) * a.B + b) * a.Hk + hk) * kD;
-            const size_t src2 = ((size_t)((min(t2, wn1 - 1) - (L - a.N)) * a.B + b) * a.Hk + hk) * kD;
+            const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+            const size_t src2 = ((size_t)(qt0 + (min(t2, wn1 - 1) - tn0) * qts) * a.Hk + hk) * kD;
             const quant::TokenHead x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
             const quant::TokenHead x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
-            quant::quantize_token_head<PRESET>(a.wbase + ((size_t)unit * a.nblk + (t >> 4)) * L_::kBlockBytes, t & 15,
-                                               x, lane);
-            if (t2 < wn1)
-                quant::quantize_token_head<PRESET>(a.wbase + ((size_t)unit * a.nblk + (t2 >> 4)) * L_::kBlockBytes,
-                                                   t2 & 15, x2, lane);
+            uint8_t *blk = store_block(t);
+            if (blk)
+                quant::quantize_token_head<PRESET>(blk, t & 15, x, lane);
+            if (t2 < wn1) {
+                uint8_t *blk2 = store_block(t2);
+                if (blk2)
+                    quant::quantize_token_head<PRESET>(blk2, t2 & 15, x2, lane);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
     for (; issued < min(kInitTiles, ntile); ++issued)
-        issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + issued * kSlotBytes, voff, voff_last, lane);
+        issue(issued, ring_lds + issued * kSlotBytes);
 
     // 4. state set-up while the loads are in flight
     int erow[NQT]; // effective end of this lane's query rows (causal window)
@@ -526,10 +617,10 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     for (int qt = 0; qt < NQT; ++qt) {
         const int rr = row0 + 32 * qt + col;
         const int n = row_token(rr);
-        erow[qt] = (rr < a.R) ? (a.causal ? min(L - a.N + n + 1, L) : L) : 0;
+        erow[qt] = (rr < Rb) ? (a.causal ? min(L - nq + n + 1, L) : L) : 0;
     }
     // every row sees every token below emin: tiles ending there need no mask
-    const int emin = a.causal ? (L - a.N + 1) : L;
+    const int emin = a.causal ? (L - nq + 1) : L;
     floatx16 acc[4][NQT];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -585,7 +676,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
                 qh[c / 2 + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale)});
             }
         }
-        if (row0 + rr >= a.R) {
+        if (row0 + rr >= Rb) {
 #pragma unroll
             for (int j = 0; j < CPT / 2; ++j)
                 qh[j] = 0u;
@@ -669,8 +760,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     auto refill = [&](int i) {
         if (issued < ntile && issued <= i + DEPTH) {
             wait_lgkm0(); // the slot's LDS reads are complete
-            issue_tile<PRESET>(ubase, kt0 + issued, a.nblk, ring_lds + (issued % DEPTH) * kSlotBytes, voff,
-                               voff_last, lane);
+            issue(issued, ring_lds + (issued % DEPTH) * kSlotBytes);
             ++issued;
         }
     };
@@ -851,7 +941,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             xbuf[((wave * 4 + aa) * 4 + dt) * 64 + lane] =
                 make_float4(acc[dt][0][4 * aa], acc[dt][0][4 * aa + 1], acc[dt][0][4 * aa + 2], acc[dt][0][4 * aa + 3]);
     __syncthreads();
-    const int lrow = col, row = row0 + lrow;
+    const int lrow = col;
     float M = -__builtin_inff();
     float4 ms[kWaves];
 #pragma unroll
@@ -930,10 +1020,10 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             const int f4 = threadIdx.x + 256 * k; // float4 index, row-major
             const int r = f4 >> 5, c = (f4 & 31) * 4;
             const int grow = row0 + r;
-            if (grow >= a.R)
+            if (grow >= Rb)
                 continue;
             const int n = row_token(grow), g = grow - n * a.G;
-            float *dst = a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD;
+            float *dst = a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD;
             *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
         }
     } else {
@@ -978,7 +1068,16 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
     const int lrow = ((blk & 3) << 3) + (threadIdx.x >> 5); // row within the tile
     const int unit = grp / a.nrt, rt = grp % a.nrt;
     const int row = 32 * rt + lrow;
-    if (unit >= a.B * a.Hk || row >= a.R)
+    if (unit >= a.B * a.Hk)
+        return;
+    const int b = unit / a.Hk, hk = unit % a.Hk;
+    int nq = a.N, qt0 = b, qts = a.B;
+    if (a.cu_q) {
+        qt0 = a.cu_q[b];
+        nq = min(max(a.cu_q[b + 1] - qt0, 0), a.N);
+        qts = 1;
+    }
+    if (row >= a.G * nq)
         return;
     const int d = (threadIdx.x & 31) * 4;
     const size_t base = (size_t)grp * a.nsplit * 32 + lrow;
@@ -1024,24 +1123,28 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
         }
     }
     const float inv = (den != 0.0f) ? 1.0f / den : __builtin_nanf("");
-    const int b = unit / a.Hk, hk = unit % a.Hk;
     const int n = (int)(((float)row + 0.5f) * __builtin_amdgcn_rcpf((float)a.G)), g = row - n * a.G;
-    *reinterpret_cast<float4 *>(a.out + ((size_t)(n * a.B + b) * a.Hq + hk * a.G + g) * kD + d) =
+    *reinterpret_cast<float4 *>(a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD + d) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 
 } // namespace
 
-hipError_t launch_verify(int preset, int nqt, const VerifyArgs &a, hipStream_t s)
+hipError_t launch_verify(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * a.nrt)), block(256);
-    if (nqt != 1)
-        return hipErrorInvalidValue;
-    if (preset == kPresetK3V4)
-        hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1>), grid, block, 0, s, a);
+    if (preset == kPresetK3V4) {
+        if (paged)
+            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1, false>), grid, block, 0, s, a);
+    } else {
+        if (paged)
+            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1, false>), grid, block, 0, s, a);
+    }
     if (hipGetLastError() != hipSuccess)
         return hipErrorLaunchFailure;
     if (a.nsplit > 1) {

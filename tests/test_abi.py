@@ -101,7 +101,7 @@ def test_verify_rejects_bad_arguments():
     assert call(sc=float("inf")) == -1
     assert call(sc=float("nan")) == -1
     assert call(Hq=15) == -2            # Hq % Hk != 0
-    assert call(n=9) == -2              # (16/2) * 9 = 72 rows > 64
+    assert call(n=129) == -2            # more than 128 queries per sequence
     assert call(Q=4104) == -3           # Q must be 16-byte aligned
     assert call(out=4100) == -3
     n = ctypes.c_size_t(7)
@@ -122,4 +122,87 @@ def test_store_verify_rejects_bad_arguments():
     assert call(V=None) == -1
     assert call(K=4097) == -3           # K must be 2-byte aligned
     assert call(Q=None) == -1
-    assert call(n=9) == -2
+    assert call(n=129) == -2
+
+
+def test_row_limit():
+    L = tq.lib()
+    d = _desc(Hk=1)
+    # 128 query heads per KV head x 65 queries = 8320 rows > 8192
+    assert L.tqkv_verify(ctypes.byref(d), 4096, 0, 4096, 65, 128, 1, 0, 0.0, 4096, None, 0, None) == -2
+    n = ctypes.c_size_t(0)
+    assert L.tqkv_verify_workspace_bytes(ctypes.byref(d), 65, 128, 0, ctypes.byref(n)) == -2
+
+
+def _pdesc(**kw):
+    d = dict(preset=tq.K8V4, Hk=2, D=128, num_pages=64, base=4096, bt=8192, B=2, max_pages=8)
+    d.update(kw)
+    return tq._PagedDesc(d["preset"], d["Hk"], d["D"], d["num_pages"], d["base"], d["bt"], d["B"],
+                         d["max_pages"])
+
+
+def test_paged_sizes():
+    assert tq.tqkv_paged_cache_bytes(tq.K3V4_NC, 4, 128, 2048) == 2048 * 4 * 1920
+    assert tq.tqkv_paged_cache_bytes(tq.K8V4, 4, 128, 2048) == 2048 * 4 * 3168
+    assert tq.tqkv_paged_cache_bytes(tq.K8V4, 4, 64, 2048) == 0
+    assert tq.tqkv_paged_cache_bytes(tq.K8V4, 0, 128, 2048) == 0
+    assert tq.tqkv_paged_cache_bytes(tq.K8V4, 1, 128, 0) == 0
+    assert tq.tqkv_paged_cache_bytes(9, 1, 128, 1) == 0
+
+
+def test_paged_store_rejects_bad_arguments():
+    L = tq.lib()
+
+    def call(d, K=4096, V=4096, sm=4096, T=1):
+        return L.tqkv_paged_store(ctypes.byref(d) if d is not None else None, K, V, sm, T, None)
+
+    assert call(None) == -1
+    assert call(_pdesc(preset=5)) == -1
+    assert call(_pdesc(num_pages=0)) == -1
+    assert call(_pdesc(base=0)) == -1
+    assert call(_pdesc(D=96)) == -2
+    assert call(_pdesc(base=4104)) == -3
+    assert call(_pdesc(), sm=None) == -1
+    assert call(_pdesc(), T=-1) == -1
+    assert call(_pdesc(), sm=4098) == -3
+    assert call(_pdesc(), K=4097) == -3
+    # the store needs no block table
+    assert call(_pdesc(bt=None, B=0, max_pages=0), K=None, V=None, sm=None, T=0) == 0
+
+
+def test_paged_verify_rejects_bad_arguments():
+    L = tq.lib()
+
+    def verify(d, n=8, Hq=16):
+        return L.tqkv_paged_verify(ctypes.byref(d), 4096, 0, 4096, n, Hq, 1, 0, 0.0, 4096, None, 0, None)
+
+    assert verify(_pdesc(bt=None)) == -1
+    assert verify(_pdesc(B=0)) == -1
+    assert verify(_pdesc(max_pages=0)) == -1
+    assert verify(_pdesc(max_pages=524289)) == -2
+    assert verify(_pdesc(bt=8194)) == -3
+    assert verify(_pdesc(), Hq=15) == -2
+    assert verify(_pdesc(), n=129) == -2
+    n = ctypes.c_size_t(3)
+    assert L.tqkv_paged_verify_workspace_bytes(ctypes.byref(_pdesc(bt=None)), 8, 16, 0, ctypes.byref(n)) == -1
+    assert n.value == 0
+    assert L.tqkv_paged_verify_num_splits(ctypes.byref(_pdesc(bt=None)), 8, 16, 0) == 0
+    d = _pdesc()
+    assert L.tqkv_paged_store_verify(ctypes.byref(d), None, 4096, 4096, 0, 4096, 8, 16, 1, 0, 0.0, 4096,
+                                     None, 0, None) == -1
+    assert L.tqkv_paged_verify_varlen(ctypes.byref(d), 4096, 0, None, 8, 4096, 16, 1, 0, 0.0, 4096,
+                                      None, 0, None) == -1
+
+
+def test_varlen_rejects_bad_arguments():
+    L = tq.lib()
+    d = _desc(Hk=2)
+
+    def call(cu=4096, mq=8, Q=4096):
+        return L.tqkv_verify_varlen(ctypes.byref(d), Q, 0, cu, mq, 4096, 16, 1, 0, 0.0, 4096, None, 0, None)
+
+    assert call(cu=None) == -1
+    assert call(mq=0) == -1
+    assert call(mq=129) == -2
+    assert call(cu=4098) == -3
+    assert call(Q=4100) == -3
