@@ -13,7 +13,9 @@ steps are captured in one HIP graph (launch-bound loop) and replayed once,
 bracketed by device synchronisation; the eager (non-graph) rate is reported
 beside it.
 
-Output: one JSON line (see the design doc for the field definitions).
+Output: one JSON line: the step rate (value, effective KV GB/s), per-call
+times of every entry point timed, the roofline of the verify launch and the
+CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -60,7 +62,7 @@ def kernel_source_digest():
     readings taken on another version of the kernel are not reported."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("verify.hip", "quant.h", "common.h", "codebook.h"):
+    for name in ("verify.hip", "quant.h", "common.h", "codebook.h", "api.hip"):
         with open(os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -108,7 +110,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the verify path needs no "
-              "communication; see DESIGN.md for how it would shard). Use --gpus 1.",
+              "communication: every (sequence, KV head) is independent). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -116,7 +118,7 @@ def main():
 
     import quantized_kv_attention_amd as tq
     from tests import synth
-    from tests.gputil import gpu_store_all, to_dev
+    from tests.gputil import gpu_paged_store_all, gpu_store_all, page_table, to_dev
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -134,6 +136,13 @@ def main():
     caches = [base]
     for _ in range(R - 1):
         caches.append(tq.Cache(preset, B, Hk, S, device=dev, buffer=base.buffer.clone()))
+    # the same tokens in a paged pool (random page order), R replicas
+    table = page_table(B, S)
+    pbase = gpu_paged_store_all(cfg, inp, table, device=dev)
+    pools = [pbase]
+    for _ in range(R - 1):
+        pools.append(tq.PagedCache(preset, Hk, pbase.num_pages, device=dev, buffer=pbase.buffer.clone(),
+                                   block_table=pbase.block_table))
     si, po = synth.token_lists(B, S, S - N, S)
     Kn = to_dev(synth.rows(inp["K"], S - N, S), dev)
     Vn = to_dev(synth.rows(inp["V"], S - N, S), dev)
@@ -144,7 +153,8 @@ def main():
     Q = to_dev(inp["Q"], dev)
     sl = to_dev(inp["seq_lens"], dev)
     out = torch.empty((N, B, Hq, 128), dtype=torch.float32, device=dev)
-    ws_bytes = tq.tqkv_verify_workspace_bytes(base, N, Hq, args.num_splits)
+    ws_bytes = max(tq.tqkv_verify_workspace_bytes(base, N, Hq, args.num_splits),
+                   tq.tqkv_paged_verify_workspace_bytes(pbase, N, Hq, args.num_splits))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     splits = tq.tqkv_verify_num_splits(base, N, Hq, args.num_splits)
     torch.cuda.synchronize()
@@ -160,6 +170,14 @@ def main():
     def step(i):
         tq.tqkv_store_verify(caches[i % R], Kf, Vf, Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
                              out=out, workspace=ws)
+
+    def verify_paged(i):
+        tq.tqkv_paged_verify(pools[i % R], Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
+                             out=out, workspace=ws)
+
+    def step_paged(i):
+        tq.tqkv_paged_store_verify(pools[i % R], Kf, Vf, Q, sl, N, Hq, cfg["causal"],
+                                   num_splits=args.num_splits, out=out, workspace=ws)
 
     def step_unfused(i):
         store(i)
@@ -194,6 +212,8 @@ def main():
     g_verify = capture(verify, args.kernel_calls)
     g_store = capture(store, args.kernel_calls)
     g_unfused = capture(step_unfused, args.kernel_calls)
+    g_vpaged = capture(verify_paged, args.kernel_calls)
+    g_spaged = capture(step_paged, args.kernel_calls)
     g_warm.replay()
     torch.cuda.synchronize()
 
@@ -210,6 +230,8 @@ def main():
     verify_ms = min(time_graph(g_verify) for _ in range(3)) / args.kernel_calls
     store_ms = min(time_graph(g_store) for _ in range(3)) / args.kernel_calls
     unfused_ms = min(time_graph(g_unfused) for _ in range(3)) / args.kernel_calls
+    vpaged_ms = min(time_graph(g_vpaged) for _ in range(3)) / args.kernel_calls
+    spaged_ms = min(time_graph(g_spaged) for _ in range(3)) / args.kernel_calls
     # warm (MALL-resident) verify: one replica only
     g_warmv = capture(lambda i: verify(0), args.kernel_calls)
     verify_warm_ms = min(time_graph(g_warmv) for _ in range(3)) / args.kernel_calls
@@ -258,6 +280,8 @@ def main():
         "us_per_store_call": round(store_ms * 1e3, 3),
         "us_per_step_store_then_verify": round(unfused_ms * 1e3, 3),
         "us_per_verify_call_mall_warm": round(verify_warm_ms * 1e3, 3),
+        "us_per_verify_call_paged": round(vpaged_ms * 1e3, 3),
+        "us_per_step_paged": round(spaged_ms * 1e3, 3),
         "us_per_step_eager": round(eager_ms * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,
         "roofline": {

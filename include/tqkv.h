@@ -37,8 +37,8 @@
  * correction, fp16 value scale, fp16 value zero); a k8v4 block is 3168 B
  * (198 B per token: 128 B of FP8 E4M3 key codes, 64 B of value codes, fp16
  * key scale, value scale, value zero).  The exact byte and bit placement is
- * specified in the design notes of this repository; the stored bytes of a
- * token depend only on that token's K and V.
+ * given by the byte offsets in the library source (common.h); the stored
+ * bytes of a token depend only on that token's K and V.
  *
  * Paged cache (tqkv_paged_cache).  The cache the pages measure is a pool of
  * blocks of 16 tokens, each holding those tokens for every KV head ("Roofline"

@@ -23,7 +23,7 @@
  *    TL;DR: the PoC shape N_spec=8, B=4, Hq=32, Hk=4, D=128, seqlen=8192.
  *
  * Where the pages leave a step open, this file takes one explicit reading;
- * every reading is tagged [Rn] and listed in the design notes.  Arithmetic:
+ * every reading is tagged [Rn] where it is taken.  Arithmetic:
  *  - store: IEEE binary32, round-to-nearest-even, no FMA contraction
  *    (compile with -ffp-contract=off), correctly rounded sqrtf and '/'.
  *    Codes are integers decided in binary32, so they are exact by definition.

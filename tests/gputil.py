@@ -32,6 +32,31 @@ def gpu_store_all(cfg: dict, inp: dict, device="cuda", max_seq: int | None = Non
     return cache
 
 
+def page_table(B: int, S: int, seed: int = 1234) -> np.ndarray:
+    """A block table [B, ceil(S/16)] holding a random permutation of the
+    pool's B * ceil(S/16) pages (neighbouring blocks in unrelated pages)."""
+    nblk = (S + 15) // 16
+    perm = np.random.default_rng(seed).permutation(B * nblk).astype(np.int32)
+    return perm.reshape(B, nblk)
+
+
+def gpu_paged_store_all(cfg: dict, inp: dict, table: np.ndarray, device="cuda",
+                        chunk_tokens: int = 1 << 22) -> tq.PagedCache:
+    """Store every token of every sequence into a pool of table.size pages
+    with tqkv_paged_store (slot = table[b, t // 16] * 16 + t % 16)."""
+    B, S, Hk = cfg["B"], cfg["S"], cfg["Hk"]
+    pc = tq.PagedCache(cfg["preset"], Hk, int(table.size), device=device, block_table=to_dev(table, device))
+    per = max(1, chunk_tokens // (B * Hk * 128))
+    for s0 in range(0, S, per):
+        s1 = min(S, s0 + per)
+        si, po = synth.token_lists(B, S, s0, s1)
+        slots = (table[si, po // 16] * 16 + po % 16).astype(np.int32)
+        K = to_dev(synth.rows(inp["K"], s0, s1), device)
+        V = to_dev(synth.rows(inp["V"], s0, s1), device)
+        tq.tqkv_paged_store(pc, K, V, to_dev(slots, device))
+    return pc
+
+
 def oracle_unit(oracle, cfg: dict, inp: dict, b: int, hk: int, heads=None, causal=None):
     """Oracle output rows [N, nh, 128] (float64) of KV head hk of sequence b,
     for query heads `heads` (default: the whole group), from the raw inputs."""

@@ -9,7 +9,8 @@ as ``[B, S, Hk, 128]`` (every token of every sequence); Q as
 ``[N, B, Hq, 128]``.  Every sequence holds ``S`` tokens (the N speculative
 tokens included), so ``seq_lens[b] = S`` and ``cached_len = S - N``.
 
-Workloads (names describe the shapes; see the design doc for their sources):
+Workloads (names describe the shapes: the pages' PoC shape, a plain decode
+and a long-context step):
   tiny_k8v4        N=8 B=1  Hq=8  Hk=1 S=512    causal, Q/K/V fp16, seed 0
   poc_k8v4         N=8 B=4  Hq=32 Hk=4 S=8192   causal, Q fp32,     seed 1
   poc_k3v4_nc      same shape and inputs as poc_k8v4,                 seed 1
