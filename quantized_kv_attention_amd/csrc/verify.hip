@@ -605,7 +605,11 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
                     quant::quantize_token_head<PRESET>(blk2, t2 & 15, x2, lane);
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // every store of this work-group complete (and, the wait being one
+        // the compiler sees, no input load left pending in its books: it
+        // would otherwise wait for the query and the first ring tiles before
+        // reusing those registers)
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     for (; issued < min(kInitTiles, ntile); ++issued)
@@ -1086,19 +1090,21 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
     for (int s0 = 0; s0 < a.nsplit; s0 += kCombineChunk) {
         float2 ml[kCombineChunk];
         float4 v[kCombineChunk];
+        // every load of the chunk is issued before any is used (ranges past
+        // the last re-read the last one and get weight 0): a guarded load
+        // per range would cost one memory round trip each
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j) {
-            if (s0 + j < a.nsplit) {
-                const size_t ix = base + (size_t)(s0 + j) * 32;
-                ml[j] = a.part_ml[ix];
-                const uint2 hv = *reinterpret_cast<const uint2 *>(a.part_o + ix * kD + d);
-                const half2_t h0 = __builtin_bit_cast(half2_t, hv.x), h1 = __builtin_bit_cast(half2_t, hv.y);
-                v[j] = make_float4((float)h0[0], (float)h0[1], (float)h1[0], (float)h1[1]);
-            } else {
-                ml[j] = make_float2(-__builtin_inff(), 0.0f);
-                v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            const size_t ix = base + (size_t)min(s0 + j, a.nsplit - 1) * 32;
+            ml[j] = a.part_ml[ix];
+            const uint2 hv = *reinterpret_cast<const uint2 *>(a.part_o + ix * kD + d);
+            const half2_t h0 = __builtin_bit_cast(half2_t, hv.x), h1 = __builtin_bit_cast(half2_t, hv.y);
+            v[j] = make_float4((float)h0[0], (float)h0[1], (float)h1[0], (float)h1[1]);
         }
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j)
+            if (s0 + j >= a.nsplit)
+                ml[j] = make_float2(-__builtin_inff(), 0.0f);
         float Mc = M;
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j)
