@@ -110,16 +110,24 @@ int row_tiles(int rows) { return (rows + 31) / 32; }
 // VGPRs), so a work-group covers at most 256 tiles of 32 tokens.
 constexpr int kPagedTilesPerGroup = 256;
 
-// Key-range partitions per (b, hk): two work-groups of 4 wavefronts per
-// compute unit overall, at least one 32-token tile per wavefront.
+// 32-row tiles per work-group: units with more than one tile of query rows
+// take them in pairs (one 64-row work-group per compute unit, every key
+// tile dequantised once for all 64 rows); otherwise one (two work-groups
+// per compute unit).
+int rows_per_group(int rows) { return row_tiles(rows) >= 2 ? 2 : 1; }
+
+// Key-range partitions per (b, hk): one compute unit's worth of work-groups
+// per compute unit overall (two 32-row or one 64-row work-group), at least
+// one 32-token tile per wavefront.
 int plan_splits(const View &c, int num_splits, int cus, int rows)
 {
-    const int units = c.B * c.Hk * row_tiles(rows);
+    const int nqt = rows_per_group(rows);
+    const int units = c.B * c.Hk * ((row_tiles(rows) + nqt - 1) / nqt);
     const int tiles = (c.max_seq + 31) / 32;
     const int max_useful = (tiles + 3) / 4;
     int s = num_splits;
     if (s <= 0)
-        s = (2 * cus + units - 1) / units;
+        s = (2 / nqt * cus + units - 1) / units;
     if (s > max_useful)
         s = max_useful;
     if (s > 1024)
@@ -279,7 +287,7 @@ int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q
     a.btab = v.btab;
     a.bstride = v.bstride;
     a.npages = v.npages;
-    if (launch_verify(v.preset, v.btab != nullptr, a, s) != hipSuccess)
+    if (launch_verify(v.preset, v.btab != nullptr, rows_per_group(R), a, s) != hipSuccess)
         return TQKV_ERR_LAUNCH;
     return TQKV_OK;
 }

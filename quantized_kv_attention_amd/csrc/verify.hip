@@ -74,15 +74,16 @@ __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // tile i has been read into registers, so kRing - 1 tiles stay in flight.
 // ---------------------------------------------------------------------------
 // The depth is chosen so that a 32-row work-group fits in 80 KiB of LDS
-// (two work-groups per compute unit).
-template <int PRESET> struct Ring;
-template <> struct Ring<kPresetK3V4> {
+// (two work-groups per compute unit); a 64-row work-group has a compute
+// unit to itself and takes twice the depth (with its 32 KiB of query rows).
+template <int PRESET, int NQT> struct Ring;
+template <int NQT> struct Ring<kPresetK3V4, NQT> {
     static constexpr int kLoads = 4; // ceil(2 * 1920 / 1024)
-    static constexpr int kDepth = 4;
+    static constexpr int kDepth = 4 * NQT;
 };
-template <> struct Ring<kPresetK8V4> {
+template <int NQT> struct Ring<kPresetK8V4, NQT> {
     static constexpr int kLoads = 7; // ceil(2 * 3168 / 1024)
-    static constexpr int kDepth = 2;
+    static constexpr int kDepth = 2 * NQT;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -153,7 +154,7 @@ __device__ inline void issue_tile(const uint8_t *ubase, int kt, int nblk, uint32
                                   uint32_t voff_last, int lane)
 {
     using L = Layout<PRESET>;
-    constexpr int LPT = Ring<PRESET>::kLoads;
+    constexpr int LPT = Ring<PRESET, 1>::kLoads;
     const uint8_t *src = ubase + (size_t)(2 * kt) * L::kBlockBytes;
     if (__builtin_expect(2 * kt + 1 < nblk, 1)) {
 #pragma unroll
@@ -177,7 +178,7 @@ __device__ inline void issue_tile_paged(const uint8_t *src0, const uint8_t *src1
                                         uint32_t voff, uint32_t voff_last, int lane)
 {
     using L = Layout<PRESET>;
-    constexpr int LPT = Ring<PRESET>::kLoads, BB = L::kBlockBytes;
+    constexpr int LPT = Ring<PRESET, 1>::kLoads, BB = L::kBlockBytes;
     constexpr int JS = BB / 1024;                      // the straddling load
     constexpr int kSplitLane = (BB - 1024 * JS) / 16; // its first lane in block 1
     static_assert(BB % 16 == 0 && kSplitLane > 0 && JS < LPT - 1, "tile split");
@@ -435,7 +436,7 @@ template <int PRESET, int NQT, bool PAGED>
 __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArgs a)
 {
     constexpr int RP = 32 * NQT; // padded rows
-    constexpr int LPT = Ring<PRESET>::kLoads, DEPTH = Ring<PRESET>::kDepth;
+    constexpr int LPT = Ring<PRESET, NQT>::kLoads, DEPTH = Ring<PRESET, NQT>::kDepth;
     constexpr int kSlotBytes = LPT * 1024;
     // query region: the unit's raw rows (fp32: 512 B, fp16: 256 B each),
     // then, in place, the fp16 operand rows (kQStride halfs each)
@@ -462,9 +463,13 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     int item = blockIdx.x;
     if ((gridDim.x & 7) == 0)
         item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    const int rt = item % a.nrt, us = item / a.nrt;
+    // a work-group covers NQT consecutive 32-row tiles of the unit (its
+    // partial states keep the per-32-row-tile layout combine_kernel reads)
+    const int nwt = (a.nrt + NQT - 1) / NQT;
+    const int rt = item % nwt, us = item / nwt;
     const int unit = us / a.nsplit, split = us % a.nsplit;
-    const int row0 = RP * rt; // first query row of this work-group
+    const int row0 = RP * rt;  // first query row of this work-group
+    const int tile0 = NQT * rt; // its first 32-row tile
     const int b = unit / a.Hk, hk = unit % a.Hk;
     const int Lr = a.seq_lens[b];
     const int L = Lr < 0 ? 0 : (Lr > a.max_seq ? a.max_seq : Lr);
@@ -928,45 +933,52 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     // w then reduces C-register quad aa = w of all four: lane (col, h) ends
     // up with row lrow = col, coordinates d = 4 (8w + 4h + j) + dt
     // (j, dt = 0..3), i.e. four float4s of the output row.
-    static_assert(NQT == 1, "one 32-row tile per work-group");
     __syncthreads(); // every wavefront is done with the ring and the query rows
-    float4 *xbuf = reinterpret_cast<float4 *>(lds);           // [w][aa][dt][lane]
+    float4 *xbuf = reinterpret_cast<float4 *>(lds);           // [w][qt][aa][dt][lane]
     float4 *sbuf = reinterpret_cast<float4 *>(lds + kXBytes); // [w][row]: m, l, z
-    {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
         // softmax sums of the two lane halves (same rows, different tokens)
-        const float ls = halves_sum(st.l[0]), zs = halves_sum(st.z[0]);
+        const float ls = halves_sum(st.l[qt]), zs = halves_sum(st.z[qt]);
         if (h == 0)
-            sbuf[wave * RP + col] = make_float4(st.m[0], ls, zs, 0.0f);
+            sbuf[wave * RP + 32 * qt + col] = make_float4(st.m[qt], ls, zs, 0.0f);
     }
 #pragma unroll
-    for (int aa = 0; aa < 4; ++aa)
+    for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            xbuf[((wave * 4 + aa) * 4 + dt) * 64 + lane] =
-                make_float4(acc[dt][0][4 * aa], acc[dt][0][4 * aa + 1], acc[dt][0][4 * aa + 2], acc[dt][0][4 * aa + 3]);
+        for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                xbuf[(((wave * NQT + qt) * 4 + aa) * 4 + dt) * 64 + lane] =
+                    make_float4(acc[dt][qt][4 * aa], acc[dt][qt][4 * aa + 1], acc[dt][qt][4 * aa + 2],
+                                acc[dt][qt][4 * aa + 3]);
     __syncthreads();
-    const int lrow = col;
-    float M = -__builtin_inff();
-    float4 ms[kWaves];
+    const int lrow = col; // row within each 32-row tile
+    float M[NQT], Ls[NQT];
+    float O[NQT][4][4]; // [qt][j][dt]: row 32 qt + lrow, coordinate 4 (8 wave + 4h + j) + dt
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        ms[w] = sbuf[w * RP + lrow];
-        M = fmaxf(M, ms[w].x);
-    }
-    float al[kWaves], Ls = 0.0f, Zs = 0.0f;
+    for (int qt = 0; qt < NQT; ++qt) {
+        float4 ms[kWaves];
+        M[qt] = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        al[w] = (ms[w].x == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms[w].x - M);
-        Ls = __builtin_fmaf(al[w], ms[w].y, Ls);
-        Zs = __builtin_fmaf(al[w], ms[w].z, Zs);
-    }
-    // normalised output O = (sum_w al_w acc_w * 2^24 (even d) or 2^20 (odd d)
-    // + Zs) / Ls: the value operand carried c * 2^-24 (even d) and 16c * 2^-24
-    // (odd d).  Ls == 0: the row saw no token here (weight 0 below, NaN if
-    // nothing else contributes); a NaN Ls propagates.
-    const float inv = (Ls != 0.0f) ? 1.0f / Ls : 0.0f;
-    float O[4][4]; // [j][dt]: coordinate 4 (8 wave + 4h + j) + dt
-    {
+        for (int w = 0; w < kWaves; ++w) {
+            ms[w] = sbuf[w * RP + 32 * qt + lrow];
+            M[qt] = fmaxf(M[qt], ms[w].x);
+        }
+        float al[kWaves], Zs = 0.0f;
+        Ls[qt] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            al[w] = (ms[w].x == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms[w].x - M[qt]);
+            Ls[qt] = __builtin_fmaf(al[w], ms[w].y, Ls[qt]);
+            Zs = __builtin_fmaf(al[w], ms[w].z, Zs);
+        }
+        // normalised output O = (sum_w al_w acc_w * 2^24 (even d) or 2^20
+        // (odd d) + Zs) / Ls: the value operand carried c * 2^-24 (even d)
+        // and 16c * 2^-24 (odd d).  Ls == 0: the row saw no token here
+        // (weight 0 below, NaN if nothing else contributes); a NaN Ls
+        // propagates.
+        const float inv = (Ls[qt] != 0.0f) ? 1.0f / Ls[qt] : 0.0f;
         float ke[kWaves], ko[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
@@ -980,7 +992,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             float o[4] = {zo, zo, zo, zo};
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                const float4 x = xbuf[((w * 4 + wave) * 4 + dt) * 64 + lane];
+                const float4 x = xbuf[(((w * NQT + qt) * 4 + wave) * 4 + dt) * 64 + lane];
                 o[0] = __builtin_fmaf(kw[w], x.x, o[0]);
                 o[1] = __builtin_fmaf(kw[w], x.y, o[1]);
                 o[2] = __builtin_fmaf(kw[w], x.z, o[2]);
@@ -988,7 +1000,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                O[j][dt] = o[j];
+                O[qt][j][dt] = o[j];
         }
     }
 
@@ -1002,21 +1014,33 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     // transposed through LDS so that every store instruction writes whole
     // 512-byte rows (full cache lines) instead of 16-byte pieces of 32 rows.
     constexpr int kOStride = kD + 4; // floats per LDS row (bank spread)
-    if (a.nsplit > 1 && wave == 0 && h == 0)
-        a.part_ml[((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP + lrow] = make_float2(M, Ls);
-    if (a.nsplit == 1 && Ls == 0.0f) {
+    // partial states of the 32-row tile t of this work-group's unit
+    auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
+    if (a.nsplit > 1 && wave == 0 && h == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int qt = 0; qt < NQT; ++qt)
+            if (tile0 + qt < a.nrt)
+                a.part_ml[part_slot(tile0 + qt) + lrow] = make_float2(M[qt], Ls[qt]);
+    }
+    if (a.nsplit == 1) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                O[j][k] = __builtin_nanf("");
+        for (int qt = 0; qt < NQT; ++qt)
+            if (Ls[qt] == 0.0f) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        O[qt][j][k] = __builtin_nanf("");
+            }
     }
     __syncthreads(); // every wavefront has read the merge buffer
-    float *ob = reinterpret_cast<float *>(lds); // [32 rows][kOStride]
+    float *ob = reinterpret_cast<float *>(lds); // [RP rows][kOStride]
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4 *>(ob + lrow * kOStride + 4 * (8 * wave + 4 * h + j)) =
-            make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(ob + (32 * qt + lrow) * kOStride + 4 * (8 * wave + 4 * h + j)) =
+                make_float4(O[qt][j][0], O[qt][j][1], O[qt][j][2], O[qt][j][3]);
     __syncthreads();
     if (a.nsplit == 1) {
 #pragma unroll
@@ -1031,11 +1055,13 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
         }
     } else {
-        _Float16 *pbase = a.part_o + ((size_t)(unit * a.nrt + rt) * a.nsplit + split) * RP * kD;
 #pragma unroll
         for (int k = 0; k < RP * kD / 8 / 256; ++k) {
             const int e8 = threadIdx.x + 256 * k; // 8-element chunk, row-major
             const int r = e8 >> 4, c = (e8 & 15) * 8;
+            if (tile0 + (r >> 5) >= a.nrt)
+                continue; // the second tile of a unit with an odd tile count
+            _Float16 *pbase = a.part_o + (part_slot(tile0 + (r >> 5)) + (r & 31)) * kD;
             const float4 x0 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
             const float4 x1 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c + 4);
             const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -1048,7 +1074,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
                 q = (xs[2 * i + 1] == xs[2 * i + 1]) ? q : xs[2 * i + 1];
                 w[i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)q});
             }
-            *reinterpret_cast<u32x4 *>(pbase + r * kD + c) = u32x4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4 *>(pbase + c) = u32x4{w[0], w[1], w[2], w[3]};
         }
     }
 }
@@ -1135,22 +1161,37 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
 }
 
 
-} // namespace
 
-hipError_t launch_verify(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
+
+template <int NQT>
+void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * a.nrt)), block(256);
+    const int nwt = (a.nrt + NQT - 1) / NQT;
+    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * nwt)), block(256);
     if (preset == kPresetK3V4) {
         if (paged)
-            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, true>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, 1, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, false>), grid, block, 0, s, a);
     } else {
         if (paged)
-            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, true>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, 1, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, false>), grid, block, 0, s, a);
     }
+}
+
+} // namespace
+
+// nqt: 32-row tiles per work-group (1: two work-groups per compute unit;
+// 2: one work-group of 64 rows per compute unit, each tile dequantised once
+// for all 64 rows)
+hipError_t launch_verify(int preset, bool paged, int nqt, const VerifyArgs &a, hipStream_t s)
+{
+    if (nqt == 2)
+        launch_verify_rows<2>(preset, paged, a, s);
+    else
+        launch_verify_rows<1>(preset, paged, a, s);
     if (hipGetLastError() != hipSuccess)
         return hipErrorLaunchFailure;
     if (a.nsplit > 1) {
