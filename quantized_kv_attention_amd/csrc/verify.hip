@@ -1016,11 +1016,16 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     constexpr int kOStride = kD + 4; // floats per LDS row (bank spread)
     // partial states of the 32-row tile t of this work-group's unit
     auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
+    // (partial states are written non-temporally: combine_kernel reads them
+    // once, from memory, and they need no write-back at the kernel boundary)
     if (a.nsplit > 1 && wave == 0 && h == 0) {
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
-            if (tile0 + qt < a.nrt)
-                a.part_ml[part_slot(tile0 + qt) + lrow] = make_float2(M[qt], Ls[qt]);
+            if (tile0 + qt < a.nrt) {
+                float *pm = reinterpret_cast<float *>(&a.part_ml[part_slot(tile0 + qt) + lrow]);
+                __builtin_nontemporal_store(M[qt], pm);
+                __builtin_nontemporal_store(Ls[qt], pm + 1);
+            }
     }
     if (a.nsplit == 1) {
 #pragma unroll
@@ -1074,7 +1079,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
                 q = (xs[2 * i + 1] == xs[2 * i + 1]) ? q : xs[2 * i + 1];
                 w[i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)q});
             }
-            *reinterpret_cast<u32x4 *>(pbase + c) = u32x4{w[0], w[1], w[2], w[3]};
+            __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(pbase + c));
         }
     }
 }
