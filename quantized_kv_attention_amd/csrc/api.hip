@@ -287,7 +287,7 @@ int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q
     a.btab = v.btab;
     a.bstride = v.bstride;
     a.npages = v.npages;
-    if (launch_verify(v.preset, v.btab != nullptr, rows_per_group(R), a, s) != hipSuccess)
+    if (launch_verify(v.preset, v.btab != nullptr, rows_per_group(R), R <= 8, a, s) != hipSuccess)
         return TQKV_ERR_LAUNCH;
     return TQKV_OK;
 }

@@ -100,6 +100,6 @@ struct VerifyArgs {
 
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
-hipError_t launch_verify(int preset, bool paged, int nqt, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const VerifyArgs &a, hipStream_t s);
 
 } // namespace tqkv

@@ -360,7 +360,9 @@ __device__ inline half8_t key_operand(const KeyRegs<PRESET> &t, int ks)
 
 // S^T = K Q^T for one tile; QB[qt][ks] is the query B operand of k-step ks
 // (coordinates 64h + 8ks + 0..7 of this lane's query row 32qt + lane%32).
-template <int PRESET, int NQT>
+// TR: the operands swap roles (the register contents are the same), giving
+// S = Q K^T: lane l holds token column l%32 and rows 8(v/4) + 4h + v%4.
+template <int PRESET, int NQT, bool TR>
 __device__ inline void qk_tile(const KeyRegs<PRESET> &k, const half8_t (&QB)[NQT][8], floatx16 (&S)[NQT])
 {
 #pragma unroll
@@ -371,7 +373,8 @@ __device__ inline void qk_tile(const KeyRegs<PRESET> &k, const half8_t (&QB)[NQT
         const half8_t A = key_operand<PRESET>(k, ks);
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
-            S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, QB[qt][ks], S[qt], 0, 0, 0);
+            S[qt] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(QB[qt][ks], A, S[qt], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_f16(A, QB[qt][ks], S[qt], 0, 0, 0);
     }
 }
 
@@ -432,9 +435,15 @@ __device__ inline half8_t hadamard_operand(int o, int ks, int h)
     return r.h;
 }
 
-template <int PRESET, int NQT, bool PAGED>
+// TR (units of at most 8 query rows, NQT = 1): the scores are computed
+// transposed (one token per lane, rows 4h + v in registers v = 0..3), so the
+// softmax of a tile touches 4 registers per lane instead of 16; P reaches
+// the P V product's B operand layout (one row per lane) through a small LDS
+// block.  The accumulators and the merge are those of the plain path.
+template <int PRESET, int NQT, bool PAGED, bool TR>
 __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArgs a)
 {
+    static_assert(!TR || NQT == 1, "the transposed path is for one row tile");
     constexpr int RP = 32 * NQT; // padded rows
     constexpr int LPT = Ring<PRESET, NQT>::kLoads, DEPTH = Ring<PRESET, NQT>::kDepth;
     constexpr int kSlotBytes = LPT * 1024;
@@ -645,6 +654,28 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         st.l[qt] = 0.0f;
         st.z[qt] = 0.0f;
     }
+    // TR state: rows 4h + v (v < 4) of this lane half; the running max is
+    // the same in every lane of the half, the sums are this lane's token's
+    // share (summed over the half at the end); ttok = the lane's token.  The
+    // running max starts at kNoMax, a finite stand-in for -inf far below any
+    // score (|q.k| * scale < 1e12 for binary16 inputs), so the first tile's
+    // rescale and a row that never sees a token need no special case
+    // (exp2(kNoMax - m) = 0, exp2(-inf - kNoMax) = 0).
+    constexpr float kNoMax = -1e30f;
+    float mT[4], lT[4], zT[4];
+    int erowT[4];
+    const int ttok = tile_token_of_row(col);
+    if constexpr (TR) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int rr = row0 + 4 * h + v;
+            const int n = row_token(rr);
+            erowT[v] = (rr < Rb) ? (a.causal ? min(L - nq + n + 1, L) : L) : 0;
+            mT[v] = kNoMax;
+            lT[v] = 0.0f;
+            zT[v] = 0.0f;
+        }
+    }
     H8 Pp[NQT][2]; // P_{i-1} * vscale: the B operands of the pending P V
     u32x4 Vp[2];   // value nibbles of tile i-1 (A operands of the pending P V)
 #pragma unroll
@@ -749,6 +780,19 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             asm volatile("" : "+a"(QB[qt][ks]));
+    // TR: each wavefront's two 32 x 32 binary16 P blocks (rows x tokens, one
+    // per tile parity; 16 KiB in all) live in the query region, free from
+    // here on (after every wavefront has read its operands).  Only rows 0..7
+    // are ever written: rows 8..31 stay zero, the B operand of the padding
+    // rows, and both blocks start as zeros (P_{-1} = 0).
+    _Float16 *ptb = reinterpret_cast<_Float16 *>(lds) + wave * 2 * 32 * 32;
+    if constexpr (TR) {
+        static_assert(kWaves * 2 * 32 * 32 * 2 <= kQRegion, "P blocks");
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            reinterpret_cast<u32x4 *>(ptb)[64 * j + lane] = u32x4{0, 0, 0, 0};
+    }
 
     // ------------------------------------------------------------ key loop
     // One step per tile i.  The scores S_i were computed by the step before
@@ -777,7 +821,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         wait_ring<LPT>(issued - 1);
         KeyRegs<PRESET> k0;
         read_keys<PRESET>(k0, ring, lane);
-        qk_tile<PRESET, NQT>(k0, QB, S);
+        qk_tile<PRESET, NQT, TR>(k0, QB, S);
     }
     auto step = [&](int i, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -903,9 +947,132 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         // 3. S_{i+1} = K_{i+1} Q^T (MFMA; the keys become operands on the way)
         KeyRegs<PRESET> kn;
         read_keys<PRESET>(kn, ring + (inext % DEPTH) * kSlotBytes, lane);
-        qk_tile<PRESET, NQT>(kn, QB, S);
+        qk_tile<PRESET, NQT, TR>(kn, QB, S);
         Vp[0] = vr.v[0];
         Vp[1] = vr.v[1];
+        refill(i);
+    };
+
+    // TR step i (the scores S_i, transposed, were computed by the step
+    // before):
+    //   1. masks them and checks whether any row's scores exceed its max by
+    //      more than the slack (rare after the first tile); if so the row
+    //      maxima move (cross-lane max over the lane half) and everything
+    //      relative to the old maxima shrinks;
+    //   2. adds P_{i-1} V_{i-1} (MFMA; P_{i-1} * vscale read back from its
+    //      LDS block as the B operand, one row per lane) while S_i becomes
+    //      P_i (4 exponentials per lane), the sums l, z and P_i * vscale,
+    //      written to this tile's LDS block;
+    //   3. computes S_{i+1} = Q K_{i+1}^T.
+    auto read_pblock = [&](int parity, H8 (&Pq)[2]) {
+        const _Float16 *pb = ptb + parity * 1024 + col * 32 + 8 * h;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            Pq[s].h = *reinterpret_cast<const half8_t *>(pb + 16 * s);
+    };
+    auto step_tr = [&](int i, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int tok0 = (kt0 + i) * kTile;
+        int inext = i;
+        if (i + 1 < ntile) {
+            wait_ring<LPT>(issued - i - 2);
+            inext = i + 1;
+        }
+        const uint8_t *slot = ring + (i % DEPTH) * kSlotBytes;
+        // value nibbles of tile i (A operands of its P V, next step) and the
+        // value scale / zero of this lane's token
+        u32x4 vn[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            vn[s] = *reinterpret_cast<const u32x4 *>(slot + s * L_::kBlockBytes + L_::kValOff + (2 * col + h) * 16);
+        const uint8_t *fb = slot + (ttok >> 4) * L_::kBlockBytes + 2 * (ttok & 15);
+        float vsc = h2f(*reinterpret_cast<const uint16_t *>(fb + L_::kVScale));
+        float vze = h2f(*reinterpret_cast<const uint16_t *>(fb + L_::kVZero));
+        H8 Pq[2];
+        read_pblock((i - 1) & 1, Pq);
+
+        // 1. masked scores; lazy rescale
+        float sv[4], dv[4]; // scores, and scores relative to the running max
+        bool grow = false;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            sv[v] = S[0][v];
+            if constexpr (MASKED) {
+                if (tok0 + ttok >= erowT[v])
+                    sv[v] = -__builtin_inff();
+            }
+            dv[v] = sv[v] - mT[v];
+            grow |= dv[v] > kRescaleSlack;
+        }
+        if (__builtin_expect(__any(grow), 0)) {
+            float alphaT[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float tm = sv[v];
+                tm = fmaxf(tm, quant::lane_xor<1>(tm, lane));
+                tm = fmaxf(tm, quant::lane_xor<2>(tm, lane));
+                tm = fmaxf(tm, quant::lane_xor<4>(tm, lane));
+                tm = fmaxf(tm, quant::lane_xor<8>(tm, lane));
+                tm = fmaxf(tm, quant::lane_xor<16>(tm, lane));
+                alphaT[v] = 1.0f;
+                if (tm > mT[v]) {
+                    alphaT[v] = __builtin_amdgcn_exp2f(mT[v] - tm); // 0 from kNoMax
+                    lT[v] *= alphaT[v];
+                    zT[v] *= alphaT[v];
+                    mT[v] = tm;
+                    dv[v] = sv[v] - tm;
+                }
+            }
+            // the accumulators and P_{i-1} hold row col: that row's factor
+            float ar = 1.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alphaT[r & 3]), 32 * (r >> 2)));
+                ar = (col == r) ? x : ar;
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt][0] *= ar;
+            const _Float16 ah = (_Float16)ar;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                Pq[s].h *= ah;
+        }
+
+        // 2. P_{i-1} V_{i-1} with the softmax of tile i in between
+        if constexpr (MASKED) {
+            // fields of tokens past the sequence end never enter (they may hold anything)
+            if (tok0 + ttok >= L) {
+                vsc = 0.0f;
+                vze = 0.0f;
+            }
+        }
+        _Float16 *pw = ptb + (i & 1) * 1024 + ttok; // row r of this tile's block: pw[32 r]
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                acc[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(Vp, dt, s), Pq[s].h, acc[dt][0], 0, 0,
+                                                                    0);
+                if (s == 0) {
+                    const int v = dt;
+                    const float pv = __builtin_amdgcn_exp2f(dv[v]);
+                    lT[v] += pv;
+                    zT[v] = __builtin_fmaf(pv, vze, zT[v]);
+                    pw[32 * (4 * h + v)] = (_Float16)(pv * vsc);
+                }
+            }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            asm volatile("" : "+v"(lT[v]), "+v"(zT[v]));
+        Vp[0] = vn[0];
+        Vp[1] = vn[1];
+        refill(i);
+
+        // 3. S_{i+1} = Q K_{i+1}^T
+        KeyRegs<PRESET> kn;
+        read_keys<PRESET>(kn, ring + (inext % DEPTH) * kSlotBytes, lane);
+        qk_tile<PRESET, NQT, TR>(kn, QB, S);
         refill(i);
     };
 
@@ -913,18 +1080,37 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     // window and the partial tail) run through the masked variant
     const int nfast = max(0, min(ntile, (emin - kt0 * kTile) / kTile));
     int i = 0;
-    for (; i < nfast; ++i)
-        step(i, std::false_type{});
-    for (; i < ntile; ++i)
-        step(i, std::true_type{});
-    // P V of the last tile
+    if constexpr (TR) {
+        for (; i < nfast; ++i)
+            step_tr(i, std::false_type{});
+        for (; i < ntile; ++i)
+            step_tr(i, std::true_type{});
+        // P V of the last tile
+        if (ntile > 0) {
+            H8 Pq[2];
+            read_pblock((ntile - 1) & 1, Pq);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
+                for (int dt = 0; dt < 4; ++dt)
+                    acc[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(Vp, dt, s), Pq[s].h, acc[dt][0], 0,
+                                                                        0, 0);
+        }
+    } else {
+        for (; i < nfast; ++i)
+            step(i, std::false_type{});
+        for (; i < ntile; ++i)
+            step(i, std::true_type{});
+        // P V of the last tile
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(Vp, dt, s), Pp[qt][s].h, acc[dt][qt], 0, 0, 0);
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(Vp, dt, s), Pp[qt][s].h,
+                                                                         acc[dt][qt], 0, 0, 0);
+    }
 
     // ---------------------------------------------------------------- merge
     // The four wavefronts hold softmax states of the same 32 rows over
@@ -936,12 +1122,35 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     __syncthreads(); // every wavefront is done with the ring and the query rows
     float4 *xbuf = reinterpret_cast<float4 *>(lds);           // [w][qt][aa][dt][lane]
     float4 *sbuf = reinterpret_cast<float4 *>(lds + kXBytes); // [w][row]: m, l, z
+    if constexpr (TR) {
+        // rows 4h + v: the sums over the half's 32 lanes (tokens); rows 8..31
+        // are padding
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        // softmax sums of the two lane halves (same rows, different tokens)
-        const float ls = halves_sum(st.l[qt]), zs = halves_sum(st.z[qt]);
-        if (h == 0)
-            sbuf[wave * RP + 32 * qt + col] = make_float4(st.m[qt], ls, zs, 0.0f);
+        for (int v = 0; v < 4; ++v) {
+            float ls = lT[v], zs = zT[v];
+            ls += quant::lane_xor<1>(ls, lane);
+            zs += quant::lane_xor<1>(zs, lane);
+            ls += quant::lane_xor<2>(ls, lane);
+            zs += quant::lane_xor<2>(zs, lane);
+            ls += quant::lane_xor<4>(ls, lane);
+            zs += quant::lane_xor<4>(zs, lane);
+            ls += quant::lane_xor<8>(ls, lane);
+            zs += quant::lane_xor<8>(zs, lane);
+            ls += quant::lane_xor<16>(ls, lane);
+            zs += quant::lane_xor<16>(zs, lane);
+            if (col == 0)
+                sbuf[wave * RP + 4 * h + v] = make_float4(mT[v], ls, zs, 0.0f);
+        }
+        if (h == 0 && col >= 8)
+            sbuf[wave * RP + col] = make_float4(-__builtin_inff(), 0.0f, 0.0f, 0.0f);
+    } else {
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            // softmax sums of the two lane halves (same rows, different tokens)
+            const float ls = halves_sum(st.l[qt]), zs = halves_sum(st.z[qt]);
+            if (h == 0)
+                sbuf[wave * RP + 32 * qt + col] = make_float4(st.m[qt], ls, zs, 0.0f);
+        }
     }
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
@@ -1168,21 +1377,21 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
 
 
 
-template <int NQT>
+template <int NQT, bool TR>
 void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
 {
     const int nwt = (a.nrt + NQT - 1) / NQT;
     const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * nwt)), block(256);
     if (preset == kPresetK3V4) {
         if (paged)
-            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, true, TR>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, false, TR>), grid, block, 0, s, a);
     } else {
         if (paged)
-            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, true, TR>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, false, TR>), grid, block, 0, s, a);
     }
 }
 
@@ -1190,13 +1399,16 @@ void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t
 
 // nqt: 32-row tiles per work-group (1: two work-groups per compute unit;
 // 2: one work-group of 64 rows per compute unit, each tile dequantised once
-// for all 64 rows)
-hipError_t launch_verify(int preset, bool paged, int nqt, const VerifyArgs &a, hipStream_t s)
+// for all 64 rows); transposed: the transposed-score path (nqt 1, at most 8
+// rows per unit)
+hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const VerifyArgs &a, hipStream_t s)
 {
     if (nqt == 2)
-        launch_verify_rows<2>(preset, paged, a, s);
+        launch_verify_rows<2, false>(preset, paged, a, s);
+    else if (transposed && a.R <= 8)
+        launch_verify_rows<1, true>(preset, paged, a, s);
     else
-        launch_verify_rows<1>(preset, paged, a, s);
+        launch_verify_rows<1, false>(preset, paged, a, s);
     if (hipGetLastError() != hipSuccess)
         return hipErrorLaunchFailure;
     if (a.nsplit > 1) {

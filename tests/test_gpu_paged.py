@@ -173,6 +173,7 @@ RAGGED = [
     dict(Hq=8, Hk=2, lens=(100, 40, 203, 8), counts=(1, 0, 17, 8)),   # 68 rows max: 3 row tiles
     dict(Hq=8, Hk=1, lens=(300, 129), counts=(128, 3)),                # 1024 rows: 32 row tiles
     dict(Hq=32, Hk=8, lens=(64, 65, 66), counts=(5, 6, 7)),            # per-sequence draft lengths
+    dict(Hq=4, Hk=2, lens=(90, 33, 7, 200), counts=(1, 4, 0, 3)),      # at most 8 rows per KV head
 ]
 
 

@@ -214,7 +214,7 @@ def test_verify_causality_and_determinism(preset):
     tq.tqkv_store(cache, to_dev(synth.rows(inp2["K"], S - 2, S)), to_dev(synth.rows(inp2["V"], S - 2, S)),
                   to_dev(si), to_dev(po))
     c = _gpu_verify(cache, cfg, inp)
-    assert np.array_equal(a[:N - 2], c[:N - 2])
+    assert np.array_equal(a[:N - 2], c[:N - 2], equal_nan=True)
     assert not np.allclose(a[N - 2:], c[N - 2:])
 
 
@@ -285,3 +285,55 @@ def test_store_verify_fused(preset, shape):
     got_cache = cache.buffer.cpu().numpy()
     assert np.array_equal(got_cache, ref_cache), "%d bytes differ" % int((got_cache != ref_cache).sum())
     assert_close(out.cpu().numpy(), ref, what="fused " + str(shape))
+
+
+# ------------------------------------------------ units of at most 8 rows ---
+# (plain decode and small groups run the transposed-score path)
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("shape", [
+    dict(N=1, Hq=1, Hk=1, B=2, S=77, causal=True),      # 1 row
+    dict(N=3, Hq=1, Hk=1, B=1, S=300, causal=True),     # 3 rows, causal window over several tiles
+    dict(N=8, Hq=2, Hk=2, B=2, S=129, causal=True),     # 8 rows (MHA speculative step)
+    dict(N=1, Hq=16, Hk=2, B=3, S=1000, causal=False),  # 8 rows, plain decode
+    dict(N=2, Hq=12, Hk=4, B=1, S=40, causal=False),    # 6 rows, partial tail tile
+], ids=lambda s: "N%d_Hq%d_Hk%d_S%d_%s" % (s["N"], s["Hq"], s["Hk"], s["S"], "c" if s["causal"] else "nc"))
+@pytest.mark.parametrize("q_dtype", [np.float32, np.float16])
+def test_verify_few_rows(preset, shape, q_dtype):
+    cfg = _small(preset, q_dtype=q_dtype, **shape)
+    inp = synth.make_inputs(cfg)
+    if cfg["B"] > 1:
+        inp["seq_lens"][1] = max(cfg["N"], cfg["S"] - 23)  # a second, shorter length
+    print("verify few rows", PNAME[preset], shape, q_dtype.__name__, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"], inp["seq_lens"],
+                        cfg["Hq"], cfg["causal"])
+    cache = gpu_store_all(cfg, inp)
+    for ns in (0, 1, 3):
+        assert_close(_gpu_verify(cache, cfg, inp, num_splits=ns), ref, what="%s splits=%d" % (shape, ns))
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_verify_few_rows_nan_and_causality(preset):
+    """8 rows (N=8, one query head per KV head): a NaN key poisons exactly the
+    rows that see it; rewriting the last two tokens leaves rows n < N-2
+    bitwise unchanged."""
+    cfg = _small(preset, B=1, Hk=1, Hq=1, N=8, S=64)
+    inp = synth.make_inputs(cfg)
+    inp["K"][0, 60, 0, 5] = np.float16(np.nan)  # position 60: row n sees 57 + n tokens
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, 1, 1, 64, inp["Q"], inp["seq_lens"], 1, True)
+    assert np.isnan(ref[4:]).all() and not np.isnan(ref[:4]).any()
+    cache = gpu_store_all(cfg, inp)
+    for ns in (1, 2):
+        assert_close(_gpu_verify(cache, cfg, inp, num_splits=ns), ref, what="nan splits=%d" % ns)
+    a = _gpu_verify(cache, cfg, inp)
+    S, N = cfg["S"], cfg["N"]
+    K2 = inp["K"].copy()
+    V2 = inp["V"].copy()
+    K2[:, S - 2:] = 1.0
+    V2[:, S - 2:] += 5
+    si, po = synth.token_lists(1, S, S - 2, S)
+    tq.tqkv_store(cache, to_dev(synth.rows(K2, S - 2, S)), to_dev(synth.rows(V2, S - 2, S)), to_dev(si), to_dev(po))
+    c = _gpu_verify(cache, cfg, inp)
+    assert np.array_equal(a[:N - 2], c[:N - 2], equal_nan=True)
