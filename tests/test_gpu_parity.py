@@ -337,3 +337,36 @@ def test_verify_few_rows_nan_and_causality(preset):
     tq.tqkv_store(cache, to_dev(synth.rows(K2, S - 2, S)), to_dev(synth.rows(V2, S - 2, S)), to_dev(si), to_dev(po))
     c = _gpu_verify(cache, cfg, inp)
     assert np.array_equal(a[:N - 2], c[:N - 2], equal_nan=True)
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["poc_k8v4", "poc_k3v4_nc"])
+def test_step_config_full(name):
+    """The steps the benchmark times, at the PoC shape, against the oracle:
+    tqkv_store_verify (the N new tokens stored in the launch) and the paged
+    verify over a pool holding the same tokens in random page order."""
+    from tests.gputil import gpu_paged_store_all, page_table
+    cfg = synth.config(name)
+    inp = synth.make_inputs(cfg)
+    N, B, Hq, Hk, S = cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"]
+    print("step", name, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(cfg["preset"], ocache, B, Hk, S, inp["Q"], inp["seq_lens"], Hq, cfg["causal"])
+    # fused step: the cached part stored first, the new tokens by the call
+    cache = tq.Cache(cfg["preset"], B, Hk, S)
+    si, po = synth.token_lists(B, S, 0, S - N)
+    tq.tqkv_store(cache, to_dev(synth.rows(inp["K"], 0, S - N)), to_dev(synth.rows(inp["V"], 0, S - N)),
+                  to_dev(si), to_dev(po))
+    Kf = to_dev(np.ascontiguousarray(inp["K"][:, S - N:S].transpose(1, 0, 2, 3)))
+    Vf = to_dev(np.ascontiguousarray(inp["V"][:, S - N:S].transpose(1, 0, 2, 3)))
+    out = tq.tqkv_store_verify(cache, Kf, Vf, to_dev(inp["Q"]), to_dev(inp["seq_lens"]), N, Hq, cfg["causal"])
+    torch.cuda.synchronize()
+    got = cache.buffer.cpu().numpy()
+    assert np.array_equal(got, ocache), "%d bytes differ" % int((got != ocache).sum())
+    assert_close(out.cpu().numpy(), ref, what=name + " fused step")
+    del cache
+    # paged pool, random page order
+    pc = gpu_paged_store_all(cfg, inp, page_table(B, S))
+    out = tq.tqkv_paged_verify(pc, to_dev(inp["Q"]), to_dev(inp["seq_lens"]), N, Hq, cfg["causal"])
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, what=name + " paged")
