@@ -122,12 +122,12 @@ int rows_per_group(int rows) { return row_tiles(rows) >= 2 ? 2 : 1; }
 int plan_splits(const View &c, int num_splits, int cus, int rows)
 {
     const int nqt = rows_per_group(rows);
-    const int units = c.B * c.Hk * ((row_tiles(rows) + nqt - 1) / nqt);
+    const long units = (long)c.B * c.Hk * ((row_tiles(rows) + nqt - 1) / nqt);
     const int tiles = (c.max_seq + 31) / 32;
     const int max_useful = (tiles + 3) / 4;
     int s = num_splits;
     if (s <= 0)
-        s = (2 / nqt * cus + units - 1) / units;
+        s = (int)((2 / nqt * cus + units - 1) / units);
     if (s > max_useful)
         s = max_useful;
     if (s > 1024)
@@ -140,6 +140,15 @@ int plan_splits(const View &c, int num_splits, int cus, int rows)
             s = need; // <= 1024 by the page limit per sequence
     }
     return s;
+}
+
+// The launches' work-group counts (verify and combine) fit a grid dimension.
+bool grid_fits(const View &c, int rows, int splits)
+{
+    const long rt = row_tiles(rows), nqt = rows_per_group(rows);
+    const long verify_groups = (long)c.B * c.Hk * splits * ((rt + nqt - 1) / nqt);
+    const long combine_groups = splits > 1 ? (long)c.B * c.Hk * rt * 4 : 0;
+    return verify_groups <= INT32_MAX && combine_groups <= INT32_MAX;
 }
 
 int check_verify_shape(const View &c, int n_spec, int Hq)
@@ -184,7 +193,10 @@ int workspace_impl(const View &v, int n_spec, int Hq, int num_splits, size_t *by
     int cus = current_device_cus();
     if (cus < 0)
         return cus;
-    *bytes = workspace_for(v, n_spec, Hq, plan_splits(v, num_splits, cus, (Hq / v.Hk) * n_spec));
+    const int rows = (Hq / v.Hk) * n_spec, splits = plan_splits(v, num_splits, cus, rows);
+    if (!grid_fits(v, rows, splits))
+        return TQKV_ERR_UNSUPPORTED;
+    *bytes = workspace_for(v, n_spec, Hq, splits);
     return TQKV_OK;
 }
 
@@ -223,6 +235,8 @@ int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q
     const int G = Hq / v.Hk;
     const int R = G * n_spec;
     const int splits = plan_splits(v, num_splits, cus, R);
+    if (!grid_fits(v, R, splits))
+        return TQKV_ERR_UNSUPPORTED;
     const size_t need = workspace_for(v, n_spec, Hq, splits);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
