@@ -23,6 +23,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -238,16 +239,27 @@ def main():
         print("bench: second replay %.3f ms" % ((time.perf_counter() - t0) * 1e3), file=sys.stderr, flush=True)
 
     # the same step graph timed with HIP events (best of 3 replays)
-    step_events_ms = min(time_graph(g_steps) for _ in range(3)) / args.steps
-    # per-launch durations with HIP events on the launch stream
-    verify_ms = min(time_graph(g_verify) for _ in range(3)) / args.kernel_calls
-    store_ms = min(time_graph(g_store) for _ in range(3)) / args.kernel_calls
-    unfused_ms = min(time_graph(g_unfused) for _ in range(3)) / args.kernel_calls
-    vpaged_ms = min(time_graph(g_vpaged) for _ in range(3)) / args.kernel_calls
-    spaged_ms = min(time_graph(g_spaged) for _ in range(3)) / args.kernel_calls
+    def median5(g, n):
+        return statistics.median(time_graph(g) for _ in range(5)) / n
+
+    step_events_ms = median5(g_steps, args.steps)
+    # per-launch durations with HIP events on the launch stream, median of 5
+    # replays of a graph of back-to-back calls
+    verify_ms = median5(g_verify, args.kernel_calls)
+    store_ms = median5(g_store, args.kernel_calls)
+    unfused_ms = median5(g_unfused, args.kernel_calls)
+    vpaged_ms = median5(g_vpaged, args.kernel_calls)
+    spaged_ms = median5(g_spaged, args.kernel_calls)
     # warm (MALL-resident) verify: one replica only
     g_warmv = capture(lambda i: verify(0), args.kernel_calls)
-    verify_warm_ms = min(time_graph(g_warmv) for _ in range(3)) / args.kernel_calls
+    verify_warm_ms = median5(g_warmv, args.kernel_calls)
+    # what a plain read+write stream reaches on this machine: device copies of
+    # 256 MB (bytes moved = 2 x 256 MB per copy), median of 5 graphs of 10
+    csrc = torch.empty(256 * 10**6, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    g_copy = capture(lambda i: cdst.copy_(csrc), 10)
+    copy_gbs = 2 * csrc.numel() / (median5(g_copy, 10) * 1e-3) / 1e9
+    del g_copy, csrc, cdst
     # eager steps, for reference
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -289,7 +301,7 @@ def main():
             "timing": "HIP graph of K steps, one replay",
         },
         "us_per_step": round(ms_per_step * 1e3, 3),
-        "us_per_step_events_best_of_3": round(step_events_ms * 1e3, 3),
+        "us_per_step_events_median_of_5": round(step_events_ms * 1e3, 3),
         "us_per_verify_call": round(verify_ms * 1e3, 3),
         "us_per_store_call": round(store_ms * 1e3, 3),
         "us_per_step_store_then_verify": round(unfused_ms * 1e3, 3),
@@ -307,6 +319,8 @@ def main():
             "traffic": recorded_traffic(args.workload),
             "kernel": "tqkv_verify: verify_kernel (+ combine_kernel when splits > 1)",
             "bytes_per_launch": kv_bytes + qo_bytes,
+            "measured_copy_GBps": round(copy_gbs, 1),
+            "frac_of_measured_copy": round(achieved / copy_gbs, 4),
         },
         "cpu_baseline": cpu,
     }

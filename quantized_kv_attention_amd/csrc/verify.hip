@@ -780,18 +780,22 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             asm volatile("" : "+a"(QB[qt][ks]));
-    // TR: each wavefront's two 32 x 32 binary16 P blocks (rows x tokens, one
-    // per tile parity; 16 KiB in all) live in the query region, free from
-    // here on (after every wavefront has read its operands).  Only rows 0..7
-    // are ever written: rows 8..31 stay zero, the B operand of the padding
-    // rows, and both blocks start as zeros (P_{-1} = 0).
-    _Float16 *ptb = reinterpret_cast<_Float16 *>(lds) + wave * 2 * 32 * 32;
+    // TR: each wavefront's two binary16 P blocks (one per tile parity) live
+    // in the query region, free from here on (after every wavefront has read
+    // its operands).  A block is 9 rows of 32 tokens: rows 0..7 are written
+    // every tile, row 8 stays zero and is the B operand of every padding row
+    // (lanes of rows 8..31 all read it: one broadcast); both blocks start as
+    // zeros (P_{-1} = 0).  Rows are kPRow = 40 halfs (80 B) apart, so the 8
+    // live rows' 16-byte reads fall on different banks (at 64 B apart they
+    // shared 4 bank groups).
+    constexpr int kPRow = 40, kPBlk = 9 * kPRow;
+    _Float16 *ptb = reinterpret_cast<_Float16 *>(lds) + wave * 2 * kPBlk;
+    const int prow = min(col, 8); // the block row this lane's B operand reads
     if constexpr (TR) {
-        static_assert(kWaves * 2 * 32 * 32 * 2 <= kQRegion, "P blocks");
+        static_assert(kWaves * 2 * kPBlk * 2 <= kQRegion && (kPBlk * 2) % 16 == 0, "P blocks");
         lds_barrier();
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            reinterpret_cast<u32x4 *>(ptb)[64 * j + lane] = u32x4{0, 0, 0, 0};
+        for (int j = lane; j < 2 * kPBlk / 8; j += 64)
+            reinterpret_cast<u32x4 *>(ptb)[j] = u32x4{0, 0, 0, 0};
     }
 
     // ------------------------------------------------------------ key loop
@@ -965,7 +969,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     //      written to this tile's LDS block;
     //   3. computes S_{i+1} = Q K_{i+1}^T.
     auto read_pblock = [&](int parity, H8 (&Pq)[2]) {
-        const _Float16 *pb = ptb + parity * 1024 + col * 32 + 8 * h;
+        const _Float16 *pb = ptb + parity * kPBlk + prow * kPRow + 8 * h;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             Pq[s].h = *reinterpret_cast<const half8_t *>(pb + 16 * s);
@@ -1047,7 +1051,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
                 vze = 0.0f;
             }
         }
-        _Float16 *pw = ptb + (i & 1) * 1024 + ttok; // row r of this tile's block: pw[32 r]
+        _Float16 *pw = ptb + (i & 1) * kPBlk + ttok; // row r of this tile's block: pw[kPRow r]
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1059,7 +1063,7 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
                     const float pv = __builtin_amdgcn_exp2f(dv[v]);
                     lT[v] += pv;
                     zT[v] = __builtin_fmaf(pv, vze, zT[v]);
-                    pw[32 * (4 * h + v)] = (_Float16)(pv * vsc);
+                    pw[kPRow * (4 * h + v)] = (_Float16)(pv * vsc);
                 }
             }
 #pragma unroll
