@@ -146,12 +146,26 @@ __device__ inline TokenHead load_token_head(const uint16_t *kp, const uint16_t *
     return TokenHead{kp[lane], kp[lane + 64], vp[lane], vp[lane + 64]};
 }
 
-// Quantise a loaded token-head into token slot tb of the 16-token cache
-// block blk.  Called by all 64 lanes of one wavefront.
+// The quantised record of one token-head, as this lane holds it before the
+// stores: 3-bit key code words (k3v4_nc) or this lane's two FP8 codes
+// (k8v4), the key metadata, this lane's value byte and the value scale /
+// zero.  Splitting computation from stores lets two token-heads' dependent
+// exchange chains run interleaved.
+struct Record {
+    uint32_t kw[2][3];  // k3v4_nc: the key code words of this lane's triple (both halves)
+    uint32_t c0, c1;    // k8v4: FP8 codes of coordinates lane, lane + 64
+    uint16_t m0, m1;    // k3v4_nc: n, gamma; k8v4: key scale
+    uint16_t sch, zh;   // value scale, zero
+    uint32_t vbyte;     // this lane's value nibble byte
+    int vpos;           // ... and its byte index p (coordinates 2p, 2p + 1)
+};
+
+// Quantise a loaded token-head (registers only).  Called by all 64 lanes of
+// one wavefront.
 template <int PRESET>
-__device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead &in, int lane)
+__device__ inline Record quantize_record(const TokenHead &in, int lane)
 {
-    using L = Layout<PRESET>;
+    Record r;
     // ---------------------------------------------------------------- keys
     float x0 = h2f_q(in.k0), x1 = h2f_q(in.k1);
     if constexpr (PRESET == kPresetK3V4) {
@@ -172,9 +186,9 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
             x0 = __fadd_rn(u, v);
             x1 = __fsub_rn(u, v);
         }
-        const float r = __fdiv_rn(1.0f, __fmul_rn(sqrt_rn(128.0f), n));
-        const int c0 = lloyd_code(__fmul_rn(x0, r));
-        const int c1 = lloyd_code(__fmul_rn(x1, r));
+        const float rr = __fdiv_rn(1.0f, __fmul_rn(sqrt_rn(128.0f), n));
+        const int c0 = lloyd_code(__fmul_rn(x0, rr));
+        const int c1 = lloyd_code(__fmul_rn(x1, rr));
         const float q0 = centroid(c0), q1 = centroid(c1);
         const float gam = __fdiv_rn(1.0f, sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(q0, q0), __fmul_rn(q1, q1)), lane)));
 
@@ -206,33 +220,25 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
 #pragma unroll
                 for (int j = 0; j < 3; ++j)
                     w[hh][j] |= lane_xor_n(w[hh][j], s, lane);
-        if ((lane & 31) == 0) {
-            const int g = lane >> 5;
-            uint32_t *kd = reinterpret_cast<uint32_t *>(blk + tb * L::kKeyBytesPerToken);
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                kd[3 * g + j] = w[0][j];
-                kd[6 + 3 * g + j] = w[1][j];
-            }
-        }
-        if (lane == 0)
-            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = f2h(n);
-        if (lane == 1)
-            *reinterpret_cast<uint16_t *>(blk + L::kMeta1 + 2 * tb) = f2h(gam);
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                r.kw[hh][j] = w[hh][j];
+        r.m0 = f2h(n);
+        r.m1 = f2h(gam);
+        r.c0 = r.c1 = 0u;
     } else {
         float amax = fmaxf(fmaxf(0.0f, fabsf(x0)), fabsf(x1));
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1)
             amax = fmaxf(amax, lane_xor_n(amax, s, lane));
         const uint16_t sh = f2h(__fdiv_rn(amax, 448.0f));
-        const float s = h2f_q(sh);
-        const uint32_t c0 = (s == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x0, s));
-        const uint32_t c1 = (s == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x1, s));
-        uint8_t *kd = blk + tb * L::kKeyBytesPerToken;
-        kd[lane] = (uint8_t)c0;
-        kd[lane + 64] = (uint8_t)c1;
-        if (lane == 0)
-            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = sh;
+        const float sc = h2f_q(sh);
+        r.c0 = (sc == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x0, sc));
+        r.c1 = (sc == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x1, sc));
+        r.m0 = sh;
+        r.m1 = 0;
     }
 
     // -------------------------------------------------------------- values
@@ -257,13 +263,54 @@ __device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead
     const uint32_t vc0 = vcode(v0), vc1 = vcode(v1);
     const uint32_t o0 = lane_xor<1>(vc0, lane), o1 = lane_xor<1>(vc1, lane);
     // even lane: byte l/2 = (d=l | d=l+1); odd lane: byte 32 + l/2 = (d=l+63 | d=l+64)
-    const int pbyte = (lane & 1) ? (32 + (lane >> 1)) : (lane >> 1);
-    const uint32_t byte = (lane & 1) ? (o1 | (vc1 << 4)) : (vc0 | (o0 << 4));
-    blk[L::kValOff + val_byte_offset(tb, pbyte)] = (uint8_t)byte;
+    r.vpos = (lane & 1) ? (32 + (lane >> 1)) : (lane >> 1);
+    r.vbyte = (lane & 1) ? (o1 | (vc1 << 4)) : (vc0 | (o0 << 4));
+    r.sch = sch;
+    r.zh = zh;
+    return r;
+}
+
+// Write a record into token slot tb of the 16-token cache block blk (all 64
+// lanes of the wavefront that computed it).
+template <int PRESET>
+__device__ inline void store_record(uint8_t *blk, int tb, const Record &r, int lane)
+{
+    using L = Layout<PRESET>;
+    if constexpr (PRESET == kPresetK3V4) {
+        if ((lane & 31) == 0) {
+            const int g = lane >> 5;
+            uint32_t *kd = reinterpret_cast<uint32_t *>(blk + tb * L::kKeyBytesPerToken);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                kd[3 * g + j] = r.kw[0][j];
+                kd[6 + 3 * g + j] = r.kw[1][j];
+            }
+        }
+        if (lane == 0)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = r.m0;
+        if (lane == 1)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta1 + 2 * tb) = r.m1;
+    } else {
+        uint8_t *kd = blk + tb * L::kKeyBytesPerToken;
+        kd[lane] = (uint8_t)r.c0;
+        kd[lane + 64] = (uint8_t)r.c1;
+        if (lane == 0)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = r.m0;
+    }
+    blk[L::kValOff + val_byte_offset(tb, r.vpos)] = (uint8_t)r.vbyte;
     if (lane == 2)
-        *reinterpret_cast<uint16_t *>(blk + L::kVScale + 2 * tb) = sch;
+        *reinterpret_cast<uint16_t *>(blk + L::kVScale + 2 * tb) = r.sch;
     if (lane == 3)
-        *reinterpret_cast<uint16_t *>(blk + L::kVZero + 2 * tb) = zh;}
+        *reinterpret_cast<uint16_t *>(blk + L::kVZero + 2 * tb) = r.zh;
+}
+
+// Quantise a loaded token-head into token slot tb of the 16-token cache
+// block blk.  Called by all 64 lanes of one wavefront.
+template <int PRESET>
+__device__ inline void quantize_token_head(uint8_t *blk, int tb, const TokenHead &in, int lane)
+{
+    store_record<PRESET>(blk, tb, quantize_record<PRESET>(in, lane), lane);
+}
 
 } // namespace quant
 } // namespace tqkv

@@ -611,12 +611,23 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             const quant::TokenHead x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
             const quant::TokenHead x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
             uint8_t *blk = store_block(t);
-            if (blk)
-                quant::quantize_token_head<PRESET>(blk, t & 15, x, lane);
             if (t2 < wn1) {
+                // both records first (two independent exchange chains the
+                // compiler interleaves), then the stores
+                const quant::Record r1 = quant::quantize_record<PRESET>(x, lane);
+                const quant::Record r2 = quant::quantize_record<PRESET>(x2, lane);
                 uint8_t *blk2 = store_block(t2);
+                if (blk)
+                    quant::store_record<PRESET>(blk, t & 15, r1, lane);
                 if (blk2)
-                    quant::quantize_token_head<PRESET>(blk2, t2 & 15, x2, lane);
+                    quant::store_record<PRESET>(blk2, t2 & 15, r2, lane);
+            } else {
+                // (the second token-head's loads are consumed all the same,
+                // so that no path leaves them pending)
+                asm volatile("" ::"v"(x2.k0), "v"(x2.k1), "v"(x2.v0), "v"(x2.v1));
+                const quant::Record r1 = quant::quantize_record<PRESET>(x, lane);
+                if (blk)
+                    quant::store_record<PRESET>(blk, t & 15, r1, lane);
             }
         }
         // every store of this work-group complete (and, the wait being one
