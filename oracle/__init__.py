@@ -28,16 +28,19 @@ _LIB = os.path.join(_HERE, "libtqoracle.so")
 
 K8V4 = 1
 K3V4_NC = 2
+K4V4_NC = 3
 D = 128
 BLOCK = 16
 
 PINS = {
     "half_to_float/float_to_half": "numpy float16 casts (library routine), exhaustive / random",
     "e4m3_decode/e4m3_encode": "torch.float8_e4m3fn casts (library routine), exhaustive / random + tie cases",
-    "codebook": "Max (1960) 8-level Gaussian table; Lloyd optimality conditions via scipy.stats.norm",
+    "codebook": "Max (1960) 8- and 16-level Gaussian tables; Lloyd optimality conditions and MSE via "
+                "scipy.stats.norm / scipy.integrate",
     "wht128": "closed form H_ij=(-1)^popcount(i&j); orthogonality; self-inverse",
     "tree_sumsq": "binary64 sum of squares within the binary32 error bound",
-    "quant_key_k3": "norm correction |khat| = n; distortion vs Gaussian-model MSE; zero vector",
+    "quant_key_k3 / quant_key_k4": "norm correction |khat| = n; distortion vs Gaussian-model MSE; nearest "
+                                   "level; zero vector",
     "quant_key_k8": "e4m3 relative error bound 2^-4; saturation never triggered",
     "quant_val": "|v - vhat| <= scale/2; endpoints hit codes 0 and 15; constant vector exact",
     "record layout": "parity unpinned (a layout choice): round trip pack/unpack and worked bytes only",
@@ -81,11 +84,14 @@ def lib() -> ctypes.CDLL:
         L.tqo_e4m3_encode.argtypes = [ctypes.c_float]
         L.tqo_e4m3_encode.restype = ctypes.c_uint8
         L.tqo_lloyd_max_unit.argtypes = [P, P, i32]
+        L.tqo_lloyd_max_unit_n.argtypes = [i32, P, P, i32]
         L.tqo_codebook.argtypes = [P, P]
+        L.tqo_codebook_n.argtypes = [i32, P, P]
         L.tqo_wht128_f32.argtypes = [P]
         L.tqo_tree_sumsq_f32.argtypes = [P]
         L.tqo_tree_sumsq_f32.restype = ctypes.c_float
         L.tqo_quant_key_k3.argtypes = [P, P, P, P, P, P]
+        L.tqo_quant_key_lm.argtypes = [i32, P, P, P, P, P, P]
         L.tqo_quant_key_k8.argtypes = [P, P, P]
         L.tqo_quant_val.argtypes = [P, P, P, P]
         L.tqo_block_bytes.argtypes = [i32]
@@ -136,19 +142,27 @@ def e4m3_encode(x: float) -> int:
 # codebook, rotation, reduction
 # ----------------------------------------------------------------------------
 
-def lloyd_max_unit(iters: int = 2000):
-    u = np.zeros(8, np.float64)
-    t = np.zeros(7, np.float64)
-    lib().tqo_lloyd_max_unit(_p(u), _p(t), iters)
+def lloyd_max_unit(iters: int = 2000, levels: int = 8):
+    """Unit-Gaussian Lloyd-Max levels[levels] and thresholds[levels - 1] (float64)."""
+    u = np.zeros(levels, np.float64)
+    t = np.zeros(levels - 1, np.float64)
+    lib().tqo_lloyd_max_unit_n(levels, _p(u), _p(t), iters)
     return u, t
 
 
-def codebook():
-    """(centroids[8], thresholds[7]) as float32 for N(0, 1/128)."""
-    c = np.zeros(8, np.float32)
-    t = np.zeros(7, np.float32)
-    lib().tqo_codebook(_p(c), _p(t))
+def codebook(levels: int = 8):
+    """(centroids[levels], thresholds[levels - 1]) as float32 for N(0, 1/128);
+    levels 8 (k3v4_nc keys) or 16 (k4v4_nc keys)."""
+    assert levels in (8, 16)
+    c = np.zeros(levels, np.float32)
+    t = np.zeros(levels - 1, np.float32)
+    lib().tqo_codebook_n(levels, _p(c), _p(t))
     return c, t
+
+
+def key_levels(preset: int) -> int:
+    """Codebook levels of a Lloyd-Max key preset (0 for FP8 keys)."""
+    return {K3V4_NC: 8, K4V4_NC: 16}.get(preset, 0)
 
 
 def wht128(x: np.ndarray) -> np.ndarray:
@@ -174,6 +188,17 @@ def quant_key_k3(k: np.ndarray):
     n = np.zeros(1, np.uint16)
     g = np.zeros(1, np.uint16)
     lib().tqo_quant_key_k3(_p(kh), _p(c), _p(t), _p(codes), _p(n), _p(g))
+    return codes, int(n[0]), int(g[0])
+
+
+def quant_key_k4(k: np.ndarray):
+    """k4v4_nc keys: codes 0..15 against the 16-level codebook, n_h, gamma_h."""
+    kh = np.ascontiguousarray(k, dtype=np.float16).view(np.uint16)
+    c, t = codebook(16)
+    codes = np.zeros(D, np.uint8)
+    n = np.zeros(1, np.uint16)
+    g = np.zeros(1, np.uint16)
+    lib().tqo_quant_key_lm(16, _p(kh), _p(c), _p(t), _p(codes), _p(n), _p(g))
     return codes, int(n[0]), int(g[0])
 
 
@@ -246,8 +271,8 @@ def store(preset: int, cache: np.ndarray, B: int, Hk: int, max_seq: int,
 
 
 def dequant(preset: int, cache: np.ndarray, Hk: int, max_seq: int, b: int, hk: int, t: int):
-    """(khat[128], vhat[128]) float64; k3v4_nc keys are in the rotated space."""
-    c, _ = codebook()
+    """(khat[128], vhat[128]) float64; Lloyd-Max keys are in the rotated space."""
+    c, _ = codebook(key_levels(preset) or 8)
     kh = np.zeros(D, np.float64)
     vh = np.zeros(D, np.float64)
     lib().tqo_dequant(preset, Hk, max_seq, _p(cache), b, hk, t, _p(c), _p(kh), _p(vh))

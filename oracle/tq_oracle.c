@@ -1,6 +1,6 @@
 /*
  * tq_oracle.c -- plain, slow CPU reference for TurboQuant speculative-decode
- * verification attention over a 3-/8-bit-key, 4-bit-value KV cache.
+ * verification attention over a 3-/4-/8-bit-key, 4-bit-value KV cache.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
  * calls this file: only the test suite, the smoke check and the benchmark's
@@ -13,7 +13,10 @@
  *    kernel" (turboquant-xpu blog, 2026-04-14), Context: keys are rotated by
  *    a Walsh-Hadamard transform and coded with a precomputed Lloyd-Max
  *    codebook, values get uniform scalar quantisation; the k3v4_nc preset is
- *    3-bit MSE keys + 4-bit values + norm correction.  Part 3: the decode
+ *    3-bit MSE keys + 4-bit values + norm correction, and the method spans
+ *    3-4 bits per coordinate (TL;DR and Context: 3-8x capacity).  The
+ *    k4v4_nc preset is the same key coder with a 16-level codebook [R23].
+ *    Part 3: the decode
  *    loop does "bit-unpack + centroid gather + norm correction" per key tile,
  *    Q arrives already rotated, online softmax over N_spec queries.  Part 4:
  *    query n of the speculative window attends to cached_len + n + 1 tokens.
@@ -39,7 +42,14 @@
 #define TQO_D 128
 #define TQO_BLOCK 16
 
-enum { TQO_K8V4 = 1, TQO_K3V4_NC = 2 };
+enum { TQO_K8V4 = 1, TQO_K3V4_NC = 2, TQO_K4V4_NC = 3 };
+
+/* Levels of the Lloyd-Max key codebook: 8 (3-bit codes) or 16 (4-bit codes);
+ * 0 for the FP8-key preset. */
+static int lm_levels(int preset)
+{
+    return preset == TQO_K3V4_NC ? 8 : (preset == TQO_K4V4_NC ? 16 : 0);
+}
 
 /* ------------------------------------------------------------------------ */
 /* binary16 <-> binary32 (IEEE 754), written out bit by bit.                 */
@@ -171,34 +181,42 @@ static double std_cond_mean(double a, double b)
     return (pa - pb) / std_mass(a, b);
 }
 
-/* Unit-variance Lloyd-Max levels u[0..7] and thresholds t[0..6] (fp64). */
-void tqo_lloyd_max_unit(double *u, double *t, int iters)
+/* Unit-variance Lloyd-Max levels u[0..nl-1] and thresholds t[0..nl-2]
+ * (fp64): Lloyd's iteration (each threshold the midpoint of its two levels,
+ * each level the mean of its cell) from evenly spaced levels 0.5 apart. */
+void tqo_lloyd_max_unit_n(int nl, double *u, double *t, int iters)
 {
-    for (int j = 0; j < 8; ++j)
-        u[j] = -1.75 + 0.5 * j; /* any ordered start converges for N(0,1) */
+    for (int j = 0; j < nl; ++j)
+        u[j] = -0.25 * (nl - 1) + 0.5 * j; /* any ordered start converges for N(0,1) */
     for (int it = 0; it < iters; ++it) {
-        for (int j = 1; j < 8; ++j)
+        for (int j = 1; j < nl; ++j)
             t[j - 1] = 0.5 * (u[j - 1] + u[j]);
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < nl; ++j) {
             double lo = (j == 0) ? -INFINITY : t[j - 1];
-            double hi = (j == 7) ? INFINITY : t[j];
+            double hi = (j == nl - 1) ? INFINITY : t[j];
             u[j] = std_cond_mean(lo, hi);
         }
     }
-    for (int j = 1; j < 8; ++j)
+    for (int j = 1; j < nl; ++j)
         t[j - 1] = 0.5 * (u[j - 1] + u[j]);
 }
 
-void tqo_codebook(float *centroids8, float *thresholds7)
+void tqo_lloyd_max_unit(double *u, double *t, int iters) { tqo_lloyd_max_unit_n(8, u, t, iters); }
+
+/* The N(0, 1/128) codebook of nl levels (8 or 16) as binary32: levels
+ * u_j / sqrt(128), thresholds t_j / sqrt(128) [R4]. */
+void tqo_codebook_n(int nl, float *centroids, float *thresholds)
 {
-    double u[8], t[7];
-    tqo_lloyd_max_unit(u, t, 2000);
+    double u[16], t[15];
+    tqo_lloyd_max_unit_n(nl, u, t, 2000);
     const double s = sqrt(128.0);
-    for (int j = 0; j < 8; ++j)
-        centroids8[j] = (float)(u[j] / s);
-    for (int j = 0; j < 7; ++j)
-        thresholds7[j] = (float)(t[j] / s);
+    for (int j = 0; j < nl; ++j)
+        centroids[j] = (float)(u[j] / s);
+    for (int j = 0; j < nl - 1; ++j)
+        thresholds[j] = (float)(t[j] / s);
 }
+
+void tqo_codebook(float *centroids8, float *thresholds7) { tqo_codebook_n(8, centroids8, thresholds7); }
 
 /* ------------------------------------------------------------------------ */
 /* Walsh-Hadamard transform (Sylvester order) and the fixed summation tree.  */
@@ -235,14 +253,15 @@ float tqo_tree_sumsq_f32(const float *x)
 /* Quantisers (one token-head vector of D = 128 binary16 values).            */
 /* ------------------------------------------------------------------------ */
 
-/* k3v4_nc keys: norm, rotation, 3-bit Lloyd-Max codes, norm correction.
+/* Lloyd-Max keys (k3v4_nc: nl = 8, k4v4_nc: nl = 16): norm, rotation,
+ * codes against the nl-level codebook, norm correction.
  *   n     = sqrtf(tree sum of x^2)
  *   y_i   = WHT(x)_i * r,  r = 1 / (sqrt(128) * n)          (rotated unit vector)
- *   code  = #{ j : y >= tau_j }                             [R5]
+ *   code  = #{ j : y >= tau_j }  (0 .. nl-1)                [R5]
  *   gamma = 1 / sqrtf(tree sum of c[code]^2)                [R6]
  *   stored: codes, n_h = half(n), g_h = half(gamma)
  * so that the dequantised rotated key c[code] * n * gamma has norm n. */
-void tqo_quant_key_k3(const uint16_t *kh, const float *cb, const float *th,
+void tqo_quant_key_lm(int nl, const uint16_t *kh, const float *cb, const float *th,
                       uint8_t *codes, uint16_t *n_h, uint16_t *g_h)
 {
     float x[TQO_D], z[TQO_D], chat[TQO_D];
@@ -255,7 +274,7 @@ void tqo_quant_key_k3(const uint16_t *kh, const float *cb, const float *th,
     for (int i = 0; i < TQO_D; ++i) {
         float y = z[i] * r;
         int c = 0;
-        for (int j = 0; j < 7; ++j)
+        for (int j = 0; j < nl - 1; ++j)
             if (y >= th[j])
                 c++;
         codes[i] = (uint8_t)c;
@@ -264,6 +283,12 @@ void tqo_quant_key_k3(const uint16_t *kh, const float *cb, const float *th,
     float g = 1.0f / sqrtf(tqo_tree_sumsq_f32(chat));
     *n_h = tqo_float_to_half(n);
     *g_h = tqo_float_to_half(g);
+}
+
+void tqo_quant_key_k3(const uint16_t *kh, const float *cb, const float *th,
+                      uint8_t *codes, uint16_t *n_h, uint16_t *g_h)
+{
+    tqo_quant_key_lm(8, kh, cb, th, codes, n_h, g_h);
 }
 
 /* k8v4 keys [R8]: per-token scale s = half(amax / 448), codes e4m3(x / s);
@@ -328,6 +353,11 @@ void tqo_quant_val(const uint16_t *vh, uint8_t *codes, uint16_t *scale_h, uint16
 /*   [768, 1792)  value nibbles (see val_byte_offset)                        */
 /*   [1792,1824)  n_h[16]   [1824,1856) gamma_h[16]                           */
 /*   [1856,1888)  vscale_h[16]  [1888,1920) vzero_h[16]                      */
+/* k4v4_nc block (2176 B = 16 x 136):                                        */
+/*   [0, 1024)    key nibbles, 64 B per token at tb*64 (see pack_k4_codes)   */
+/*   [1024,2048)  value nibbles                                              */
+/*   [2048,2080)  n_h[16]   [2080,2112) gamma_h[16]                           */
+/*   [2112,2144)  vscale_h[16]  [2144,2176) vzero_h[16]                      */
 /* k8v4 block (3168 B = 16 x 198):                                           */
 /*   [0, 2048)    e4m3 key codes, 128 B per token at tb*128, byte d = coord d*/
 /*   [2048,3072)  value nibbles                                              */
@@ -335,8 +365,20 @@ void tqo_quant_val(const uint16_t *vh, uint8_t *codes, uint16_t *scale_h, uint16
 /* binary16 fields and dwords are little-endian.                             */
 /* ------------------------------------------------------------------------ */
 
-size_t tqo_block_bytes(int preset) { return preset == TQO_K3V4_NC ? 1920 : 3168; }
-size_t tqo_slot_bytes(int preset) { return preset == TQO_K3V4_NC ? 120 : 198; }
+size_t tqo_slot_bytes(int preset)
+{
+    return preset == TQO_K3V4_NC ? 120 : (preset == TQO_K4V4_NC ? 136 : 198);
+}
+size_t tqo_block_bytes(int preset) { return TQO_BLOCK * tqo_slot_bytes(preset); }
+
+/* Offsets inside a block: value nibbles, then the four binary16 fields
+ * (Lloyd-Max presets: n_h, gamma_h, vscale_h, vzero_h; k8v4: kscale_h,
+ * vscale_h, vzero_h), 32 B each. */
+static size_t val_region(int preset)
+{
+    return preset == TQO_K3V4_NC ? 768 : (preset == TQO_K4V4_NC ? 1024 : 2048);
+}
+static size_t meta_region(int preset) { return val_region(preset) + 1024; }
 
 /* Value nibbles: byte p (0..63) of a token holds coordinate 2p in its low
  * and 2p+1 in its high nibble.  Byte p = 2i + e of token tb lives in dword
@@ -416,6 +458,33 @@ static void unpack_k3_codes(const uint8_t *in48, uint8_t *codes)
     }
 }
 
+/* k4 key codes of one token (128 codes of 4 bits) -> 64 bytes [R23].  The
+ * stored nibble of code c (0..15, levels ascending; the codebook is
+ * symmetric, c_(15-j) = -c_j) is sign-magnitude: bit 3 set for the
+ * negative levels (c < 8), bits 0-2 the rank of |c_c| counted from zero,
+ * i.e. nibble = c - 8 for c >= 8 and 8 + (7 - c) for c < 8.  Coordinate
+ * d = 8j + e (j in 0..15, e in 0..7) goes to byte 4j + e % 4, low nibble
+ * for e < 4 and high nibble for e >= 4. */
+static uint8_t k4_nibble(uint8_t c) { return (uint8_t)(c >= 8 ? c - 8 : 8 + (7 - c)); }
+static uint8_t k4_code(uint8_t nib) { return (uint8_t)(nib >= 8 ? 7 - (nib - 8) : nib + 8); }
+
+static void pack_k4_codes(const uint8_t *codes, uint8_t *out64)
+{
+    memset(out64, 0, 64);
+    for (int d = 0; d < TQO_D; ++d) {
+        int j = d / 8, e = d % 8;
+        out64[4 * j + e % 4] |= (uint8_t)((k4_nibble(codes[d] & 15u)) << (e < 4 ? 0 : 4));
+    }
+}
+
+static void unpack_k4_codes(const uint8_t *in64, uint8_t *codes)
+{
+    for (int d = 0; d < TQO_D; ++d) {
+        int j = d / 8, e = d % 8;
+        codes[d] = k4_code((uint8_t)((in64[4 * j + e % 4] >> (e < 4 ? 0 : 4)) & 15u));
+    }
+}
+
 static void put_u16(uint8_t *p, uint16_t v)
 {
     p[0] = (uint8_t)v;
@@ -427,7 +496,7 @@ static uint16_t get_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)
 typedef struct {
     uint8_t kcode[TQO_D];
     uint8_t vcode[TQO_D];
-    uint16_t kmeta0, kmeta1; /* k3: n_h, gamma_h; k8: kscale_h, unused */
+    uint16_t kmeta0, kmeta1; /* k3/k4: n_h, gamma_h; k8: kscale_h, unused */
     uint16_t vscale, vzero;
 } tqo_record;
 
@@ -435,18 +504,21 @@ void tqo_write_record(int preset, uint8_t *block, int tb, const uint8_t *kcode,
                       const uint8_t *vcode, uint16_t kmeta0, uint16_t kmeta1,
                       uint16_t vscale, uint16_t vzero)
 {
-    size_t voff = (preset == TQO_K3V4_NC) ? 768 : 2048;
-    if (preset == TQO_K3V4_NC) {
-        pack_k3_codes(kcode, block + (size_t)tb * 48);
-        put_u16(block + 1792 + 2 * tb, kmeta0);
-        put_u16(block + 1824 + 2 * tb, kmeta1);
-        put_u16(block + 1856 + 2 * tb, vscale);
-        put_u16(block + 1888 + 2 * tb, vzero);
-    } else {
+    size_t voff = val_region(preset), mo = meta_region(preset);
+    if (preset == TQO_K8V4) {
         memcpy(block + (size_t)tb * 128, kcode, TQO_D);
-        put_u16(block + 3072 + 2 * tb, kmeta0);
-        put_u16(block + 3104 + 2 * tb, vscale);
-        put_u16(block + 3136 + 2 * tb, vzero);
+        put_u16(block + mo + 2 * tb, kmeta0);
+        put_u16(block + mo + 32 + 2 * tb, vscale);
+        put_u16(block + mo + 64 + 2 * tb, vzero);
+    } else {
+        if (preset == TQO_K3V4_NC)
+            pack_k3_codes(kcode, block + (size_t)tb * 48);
+        else
+            pack_k4_codes(kcode, block + (size_t)tb * 64);
+        put_u16(block + mo + 2 * tb, kmeta0);
+        put_u16(block + mo + 32 + 2 * tb, kmeta1);
+        put_u16(block + mo + 64 + 2 * tb, vscale);
+        put_u16(block + mo + 96 + 2 * tb, vzero);
     }
     for (int p = 0; p < TQO_D / 2; ++p)
         block[voff + val_byte_offset(tb, p)] =
@@ -457,19 +529,22 @@ void tqo_read_record(int preset, const uint8_t *block, int tb, uint8_t *kcode,
                      uint8_t *vcode, uint16_t *kmeta0, uint16_t *kmeta1,
                      uint16_t *vscale, uint16_t *vzero)
 {
-    size_t voff = (preset == TQO_K3V4_NC) ? 768 : 2048;
-    if (preset == TQO_K3V4_NC) {
-        unpack_k3_codes(block + (size_t)tb * 48, kcode);
-        *kmeta0 = get_u16(block + 1792 + 2 * tb);
-        *kmeta1 = get_u16(block + 1824 + 2 * tb);
-        *vscale = get_u16(block + 1856 + 2 * tb);
-        *vzero = get_u16(block + 1888 + 2 * tb);
-    } else {
+    size_t voff = val_region(preset), mo = meta_region(preset);
+    if (preset == TQO_K8V4) {
         memcpy(kcode, block + (size_t)tb * 128, TQO_D);
-        *kmeta0 = get_u16(block + 3072 + 2 * tb);
+        *kmeta0 = get_u16(block + mo + 2 * tb);
         *kmeta1 = 0;
-        *vscale = get_u16(block + 3104 + 2 * tb);
-        *vzero = get_u16(block + 3136 + 2 * tb);
+        *vscale = get_u16(block + mo + 32 + 2 * tb);
+        *vzero = get_u16(block + mo + 64 + 2 * tb);
+    } else {
+        if (preset == TQO_K3V4_NC)
+            unpack_k3_codes(block + (size_t)tb * 48, kcode);
+        else
+            unpack_k4_codes(block + (size_t)tb * 64, kcode);
+        *kmeta0 = get_u16(block + mo + 2 * tb);
+        *kmeta1 = get_u16(block + mo + 32 + 2 * tb);
+        *vscale = get_u16(block + mo + 64 + 2 * tb);
+        *vzero = get_u16(block + mo + 96 + 2 * tb);
     }
     for (int p = 0; p < TQO_D / 2; ++p) {
         uint8_t by = block[voff + val_byte_offset(tb, p)];
@@ -494,9 +569,10 @@ static uint8_t *block_ptr(int preset, uint8_t *base, int Hk, int max_seq, int b,
 int tqo_store(int preset, int B, int Hk, int max_seq, uint8_t *cache, const uint16_t *K,
               const uint16_t *V, const int32_t *seq_idx, const int32_t *pos, int T)
 {
-    float cb[8], th[7];
-    if (preset == TQO_K3V4_NC)
-        tqo_codebook(cb, th);
+    float cb[16], th[15];
+    const int nl = lm_levels(preset);
+    if (nl)
+        tqo_codebook_n(nl, cb, th);
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (long th_i = 0; th_i < (long)T * Hk; ++th_i) {
@@ -510,8 +586,8 @@ int tqo_store(int preset, int B, int Hk, int max_seq, uint8_t *cache, const uint
         const uint16_t *vh = V + ((size_t)t * Hk + hk) * TQO_D;
         uint8_t kc[TQO_D], vc[TQO_D];
         uint16_t m0 = 0, m1 = 0, vs, vz;
-        if (preset == TQO_K3V4_NC)
-            tqo_quant_key_k3(kh, cb, th, kc, &m0, &m1);
+        if (nl)
+            tqo_quant_key_lm(nl, kh, cb, th, kc, &m0, &m1);
         else
             tqo_quant_key_k8(kh, kc, &m0);
         tqo_quant_val(vh, vc, &vs, &vz);
@@ -533,9 +609,10 @@ int tqo_store(int preset, int B, int Hk, int max_seq, uint8_t *cache, const uint
 int tqo_store_paged(int preset, int Hk, int num_pages, uint8_t *pool, const uint16_t *K,
                     const uint16_t *V, const int32_t *slots, int T)
 {
-    float cb[8], th[7];
-    if (preset == TQO_K3V4_NC)
-        tqo_codebook(cb, th);
+    float cb[16], th[15];
+    const int nl = lm_levels(preset);
+    if (nl)
+        tqo_codebook_n(nl, cb, th);
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (long th_i = 0; th_i < (long)T * Hk; ++th_i) {
@@ -552,8 +629,8 @@ int tqo_store_paged(int preset, int Hk, int num_pages, uint8_t *pool, const uint
         const uint16_t *vh = V + ((size_t)t * Hk + hk) * TQO_D;
         uint8_t kc[TQO_D], vc[TQO_D];
         uint16_t m0 = 0, m1 = 0, vs, vz;
-        if (preset == TQO_K3V4_NC)
-            tqo_quant_key_k3(kh, cb, th, kc, &m0, &m1);
+        if (nl)
+            tqo_quant_key_lm(nl, kh, cb, th, kc, &m0, &m1);
         else
             tqo_quant_key_k8(kh, kc, &m0);
         tqo_quant_val(vh, vc, &vs, &vz);
@@ -565,7 +642,7 @@ int tqo_store_paged(int preset, int Hk, int num_pages, uint8_t *pool, const uint
 
 /* ------------------------------------------------------------------------ */
 /* Dequantisation of one token-head (binary64).                              */
-/*   k3v4_nc: khat_rot[d] = c[code] * n_h * gamma_h  (rotated space)         */
+/*   k3v4_nc, k4v4_nc: khat_rot[d] = c[code] * n_h * gamma_h (rotated space) */
 /*   k8v4:    khat[d]     = e4m3(code) * kscale_h                            */
 /*   values:  vhat[d]     = code * vscale_h + vzero_h                        */
 /* ------------------------------------------------------------------------ */
@@ -578,7 +655,7 @@ void tqo_dequant(int preset, int Hk, int max_seq, const uint8_t *cache, int b, i
     const uint8_t *blk = block_ptr(preset, (uint8_t *)cache, Hk, max_seq, b, hk, t);
     tqo_read_record(preset, blk, t % TQO_BLOCK, kc, vc, &m0, &m1, &vs, &vz);
     double vscale = tqo_half_to_float(vs), vzero = tqo_half_to_float(vz);
-    if (preset == TQO_K3V4_NC) {
+    if (preset != TQO_K8V4) {
         double f = (double)tqo_half_to_float(m0) * (double)tqo_half_to_float(m1);
         for (int d = 0; d < TQO_D; ++d)
             khat[d] = (double)cb[kc[d]] * f;
@@ -611,7 +688,7 @@ static void hadamard_f64(const double *q, double *out)
 /*   included; cached = seq_lens[b] - N                              [R13]  */
 /*   hk = hq / (Hq/Hk)                                               [R12]  */
 /*   E(n) = causal ? min(cached + n + 1, seq_len) : seq_len                  */
-/*   s_t  = sm_scale * <q', khat_t>  for t < E (k3: q' = H q, else q' = q)   */
+/*   s_t  = sm_scale * <q', khat_t>  for t < E (k3/k4: q' = H q, k8: q' = q) */
 /*   out  = sum_t softmax(s)_t vhat_t          (two passes, no splits)       */
 /* sm_scale == 0 selects 1/sqrt(128) [R14].  out: binary64 [N, B, Hq, 128].  */
 /* ------------------------------------------------------------------------ */
@@ -623,9 +700,10 @@ int tqo_verify(int preset, int B, int Hk, int max_seq, const uint8_t *cache, con
     if (Hq % Hk != 0 || N < 1)
         return -1;
     int G = Hq / Hk;
-    float cb[8], th[7];
-    if (preset == TQO_K3V4_NC)
-        tqo_codebook(cb, th);
+    float cb[16], th[15];
+    const int nl = lm_levels(preset);
+    if (nl)
+        tqo_codebook_n(nl, cb, th);
     if (sm_scale == 0.0)
         sm_scale = 1.0 / sqrt((double)TQO_D);
     for (int b = 0; b < B; ++b)
@@ -650,7 +728,7 @@ int tqo_verify(int preset, int B, int Hk, int max_seq, const uint8_t *cache, con
                 for (int d = 0; d < TQO_D; ++d)
                     q[d] = q_dtype == 0 ? (double)((const float *)Q)[qoff + d]
                                         : (double)tqo_half_to_float(((const uint16_t *)Q)[qoff + d]);
-                if (preset == TQO_K3V4_NC)
+                if (preset != TQO_K8V4)
                     hadamard_f64(q, qp);
                 else
                     memcpy(qp, q, sizeof q);

@@ -85,9 +85,9 @@ def test_e4m3_encode_saturates_and_nan():
 
 # ----------------------------------------------------------- Lloyd-Max ---
 
-def _golden_max():
+def _golden_max(levels=8):
     vals = {}
-    with open(os.path.join(GOLDEN, "lloyd_max_gaussian_8level.txt")) as f:
+    with open(os.path.join(GOLDEN, "lloyd_max_gaussian_%dlevel.txt" % levels)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -97,16 +97,18 @@ def _golden_max():
     return vals
 
 
-def test_lloyd_max_matches_max_1960_table():
-    g = _golden_max()
-    u, t = oracle.lloyd_max_unit()
-    assert np.allclose(u[4:], g["levels"], atol=6e-4)
-    assert np.allclose(-u[:4][::-1], g["levels"], atol=6e-4)
-    assert np.allclose(t[3:], g["thresholds"], atol=6e-4)
+@pytest.mark.parametrize("levels", [8, 16])
+def test_lloyd_max_matches_max_1960_table(levels):
+    g = _golden_max(levels)
+    u, t = oracle.lloyd_max_unit(levels=levels)
+    hl = levels // 2
+    assert np.allclose(u[hl:], g["levels"], atol=6e-4)
+    assert np.allclose(-u[:hl][::-1], g["levels"], atol=6e-4)
+    assert np.allclose(t[hl - 1:], g["thresholds"], atol=6e-4)
     # distortion E[(Z - Q(Z))^2], closed form per cell
     edges = np.concatenate([[-np.inf], t, [np.inf]])
     mse = 0.0
-    for j in range(8):
+    for j in range(levels):
         a, b = edges[j], edges[j + 1]
         P = stats.norm.cdf(b) - stats.norm.cdf(a)
         pa = 0.0 if np.isinf(a) else stats.norm.pdf(a)
@@ -119,19 +121,21 @@ def test_lloyd_max_matches_max_1960_table():
     assert abs(mse - g["mse"][0]) < 2e-5
 
 
-def test_lloyd_max_optimality_conditions():
-    u, t = oracle.lloyd_max_unit()
+@pytest.mark.parametrize("levels", [8, 16])
+def test_lloyd_max_optimality_conditions(levels):
+    u, t = oracle.lloyd_max_unit(levels=levels)
     edges = np.concatenate([[-np.inf], t, [np.inf]])
-    for j in range(8):
+    for j in range(levels):
         m = stats.truncnorm.mean(edges[j], edges[j + 1])
         assert abs(m - u[j]) < 1e-12
     assert np.allclose(t, (u[:-1] + u[1:]) / 2, atol=0, rtol=0)
     assert np.allclose(u, -u[::-1], atol=1e-14)
 
 
-def test_codebook_float32_tables():
-    c, th = oracle.codebook()
-    u, t = oracle.lloyd_max_unit()
+@pytest.mark.parametrize("levels", [8, 16])
+def test_codebook_float32_tables(levels):
+    c, th = oracle.codebook(levels)
+    u, t = oracle.lloyd_max_unit(levels=levels)
     assert c.dtype == np.float32 and th.dtype == np.float32
     assert np.all(np.diff(c) > 0) and np.all(np.diff(th) > 0)
     # each table entry is the binary32 value nearest to the scaled level

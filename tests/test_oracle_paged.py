@@ -34,7 +34,7 @@ def _layout(lens, max_pages, num_pages, seed):
     return table, si, po, slots.astype(np.int32)
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 def test_paged_store_gathers_to_contiguous_store(preset):
     rng = np.random.default_rng(3)
     lens, Hk, max_pages, num_pages = [37, 16, 50], 2, 4, 19
@@ -75,7 +75,7 @@ def _contig(preset, B, Hk, S, K, V, lens):
     return cache
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 @pytest.mark.parametrize("causal", [True, False])
 def test_varlen_with_equal_counts_is_dense_verify(preset, causal):
     rng = np.random.default_rng(8)
@@ -93,7 +93,7 @@ def test_varlen_with_equal_counts_is_dense_verify(preset, causal):
     assert np.array_equal(got, dense.transpose(1, 0, 2, 3).reshape(B * N, Hq, 128))
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 def test_varlen_ragged_matches_sdpa(preset):
     """Counts 1, 0, 12, 5: each sequence's rows against SDPA over its own
     dequantised tokens with the per-row window cached_len + n + 1."""
@@ -122,7 +122,7 @@ def test_varlen_ragged_matches_sdpa(preset):
             for g in range(G):
                 hq = hk * G + g
                 qv = Q[cu[b]:cu[b + 1], hq].astype(np.float64)
-                if preset == oracle.K3V4_NC:
+                if preset != oracle.K8V4:
                     qv = qv @ H.T
                 ref = torch.nn.functional.scaled_dot_product_attention(
                     torch.tensor(qv)[None, None], Kh[None, None], Vh[None, None],

@@ -23,17 +23,23 @@ def h2f(bits):
     return float(np.array([bits], np.uint16).view(np.float16)[0])
 
 
-# ------------------------------------------------------------ k3v4_nc keys ---
+# ------------------------------------------- Lloyd-Max keys (k3 and k4) ---
 
-def test_k3_codes_are_nearest_centroid():
+# (quantiser, codebook levels, Gaussian-model distortion of Max's table)
+LM_KEYS = {"k3v4_nc": (oracle.quant_key_k3, 8, 0.03454), "k4v4_nc": (oracle.quant_key_k4, 16, 0.009497)}
+
+
+@pytest.mark.parametrize("preset", list(LM_KEYS))
+def test_lm_codes_are_nearest_centroid(preset):
     """Lloyd-Max coding of the rotated unit vector = nearest centroid, except
     within rounding distance of a threshold."""
-    c, th = oracle.codebook()
+    quant, levels, _ = LM_KEYS[preset]
+    c, th = oracle.codebook(levels)
     rng = np.random.default_rng(21)
     H = _hadamard()
     for _ in range(200):
         k = rng.standard_normal(128).astype(np.float16)
-        codes, nh, gh = oracle.quant_key_k3(k)
+        codes, nh, gh = quant(k)
         x = k.astype(np.float64)
         y = H @ x / np.linalg.norm(x)
         nearest = np.argmin(np.abs(y[:, None] - c.astype(np.float64)[None, :]), axis=1)
@@ -42,39 +48,65 @@ def test_k3_codes_are_nearest_centroid():
         assert abs(h2f(nh) - np.linalg.norm(x)) <= 2.0 ** -11 * np.linalg.norm(x)
 
 
-def test_k3_norm_correction_restores_norm():
-    c, _ = oracle.codebook()
+@pytest.mark.parametrize("preset", list(LM_KEYS))
+def test_lm_norm_correction_restores_norm(preset):
+    quant, levels, _ = LM_KEYS[preset]
+    c, _ = oracle.codebook(levels)
     rng = np.random.default_rng(22)
     for _ in range(200):
         k = (rng.standard_normal(128) * rng.uniform(0.1, 10)).astype(np.float16)
-        codes, nh, gh = oracle.quant_key_k3(k)
+        codes, nh, gh = quant(k)
         khat = c[codes].astype(np.float64) * h2f(nh) * h2f(gh)
         n = np.linalg.norm(k.astype(np.float64))
         # n and gamma are each rounded to binary16 (2^-11 relative each)
         assert abs(np.linalg.norm(khat) - n) <= 2.5 * 2.0 ** -11 * n
 
 
-def test_k3_distortion_near_gaussian_model():
+@pytest.mark.parametrize("preset", list(LM_KEYS))
+def test_lm_distortion_near_gaussian_model(preset):
     """Mean squared error of the unit-vector reconstruction (before norm
-    correction) is close to the Gaussian-model Lloyd-Max MSE 0.03454."""
-    c, _ = oracle.codebook()
+    correction) is close to the Gaussian-model Lloyd-Max MSE of Max's table
+    (0.03454 at 8 levels, 0.009497 at 16): within 6 %, the coordinates of a
+    rotated unit vector being only nearly Gaussian."""
+    quant, levels, mse = LM_KEYS[preset]
+    c, _ = oracle.codebook(levels)
     rng = np.random.default_rng(23)
     H = _hadamard()
     errs = []
     for _ in range(3000):
         k = rng.standard_normal(128).astype(np.float16)
-        codes, _, _ = oracle.quant_key_k3(k)
+        codes, _, _ = quant(k)
         x = k.astype(np.float64)
         y = H @ x / np.linalg.norm(x)
         errs.append(np.sum((y - c[codes]) ** 2))
-    assert abs(np.mean(errs) - 0.03454) < 0.002
+    assert abs(np.mean(errs) - mse) < 0.06 * mse
 
 
-def test_k3_zero_vector():
-    codes, nh, gh = oracle.quant_key_k3(np.zeros(128, np.float16))
+@pytest.mark.parametrize("preset", list(LM_KEYS))
+def test_lm_zero_vector(preset):
+    quant, levels, _ = LM_KEYS[preset]
+    codes, nh, gh = quant(np.zeros(128, np.float16))
     assert np.all(codes == 0) and nh == 0
-    c, _ = oracle.codebook()
+    c, _ = oracle.codebook(levels)
     assert h2f(gh) == pytest.approx(1 / np.sqrt(128 * c[0].astype(np.float64) ** 2), rel=1e-3)
+
+
+def test_k4_refines_k3():
+    """Sixteen levels reconstruct every key at least about as well as eight
+    and about 3.6x better on average (Max's 0.03454 / 0.009497)."""
+    c3, _ = oracle.codebook(8)
+    c4, _ = oracle.codebook(16)
+    rng = np.random.default_rng(24)
+    H = _hadamard()
+    e3, e4 = [], []
+    for _ in range(500):
+        k = rng.standard_normal(128).astype(np.float16)
+        x = k.astype(np.float64)
+        y = H @ x / np.linalg.norm(x)
+        e3.append(np.sum((y - c3[oracle.quant_key_k3(k)[0]]) ** 2))
+        e4.append(np.sum((y - c4[oracle.quant_key_k4(k)[0]]) ** 2))
+    assert np.all(np.array(e4) < np.array(e3))
+    assert 3.2 < np.mean(e3) / np.mean(e4) < 4.0
 
 
 # --------------------------------------------------------------- k8 keys ---
@@ -147,6 +179,44 @@ def _read_k3_examples():
     return out
 
 
+def _read_k4_examples():
+    out = []
+    with open(os.path.join(GOLDEN, "k4_pack_worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, cs, exp = line.split()
+            codes = np.zeros(128, np.uint8)
+            for item in cs.split(","):
+                d, cc = item.split(":")
+                if d == "*":
+                    codes[:] = int(cc)
+                else:
+                    codes[int(d)] = int(cc)
+            expected = np.zeros(64, np.uint8)
+            items = exp.split(",")
+            for item in items:
+                i, hx = item.split(":")
+                if i == "*":
+                    expected[:] = int(hx, 16)
+            for item in items:
+                i, hx = item.split(":")
+                if i != "*":
+                    expected[int(i)] = int(hx, 16)
+            out.append((name, codes, expected))
+    return out
+
+
+@pytest.mark.parametrize("example", _read_k4_examples(), ids=lambda e: e[0])
+def test_k4_pack_worked_examples(example):
+    _, codes, expected = example
+    block = np.zeros(oracle.block_bytes(oracle.K4V4_NC), np.uint8)
+    oracle.write_record(oracle.K4V4_NC, block, 0, codes, np.zeros(128, np.uint8), 0, 0, 0, 0)
+    assert np.array_equal(block[:64], expected)
+    assert not np.any(block[64:])
+
+
 @pytest.mark.parametrize("example", _read_k3_examples(), ids=lambda e: e[0])
 def test_k3_pack_worked_examples(example):
     _, codes, expected = example
@@ -162,26 +232,32 @@ def test_value_nibble_worked_examples():
             line = line.strip()
             if line and not line.startswith("#"):
                 rows.append([int(x, 16) if i == 5 else int(x) for i, x in enumerate(line.split())])
-    for preset, voff in ((oracle.K3V4_NC, 768), (oracle.K8V4, 2048)):
+    for preset, voff in ((oracle.K3V4_NC, 768), (oracle.K4V4_NC, 1024), (oracle.K8V4, 2048)):
         for tb, p, lo, hi, off, byte in rows:
             block = np.zeros(oracle.block_bytes(preset), np.uint8)
             vc = np.zeros(128, np.uint8)
             vc[2 * p], vc[2 * p + 1] = lo, hi
-            oracle.write_record(preset, block, tb, np.zeros(128, np.uint8), vc, 0, 0, 0, 0)
+            # key codes whose packed bytes are all zero (k4: code 8 is the nibble 0)
+            kc = np.full(128, 8 if preset == oracle.K4V4_NC else 0, np.uint8)
+            oracle.write_record(preset, block, tb, kc, vc, 0, 0, 0, 0)
             nz = np.nonzero(block)[0]
             assert list(nz) == ([voff + off] if byte else [])
             assert block[voff + off] == byte
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+KEY_CODES = {oracle.K8V4: 256, oracle.K3V4_NC: 8, oracle.K4V4_NC: 16}
+
+
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 def test_record_round_trip_and_slot_size(preset):
-    assert oracle.slot_bytes(preset) == (120 if preset == oracle.K3V4_NC else 198)
+    # 128 codes of 8, 3 or 4 bits + 64 B of value nibbles + 3 or 4 binary16 fields
+    assert oracle.slot_bytes(preset) == {oracle.K8V4: 198, oracle.K3V4_NC: 120, oracle.K4V4_NC: 136}[preset]
     assert oracle.block_bytes(preset) == 16 * oracle.slot_bytes(preset)
     rng = np.random.default_rng(26)
     block = np.zeros(oracle.block_bytes(preset), np.uint8)
     recs = []
     for tb in rng.permutation(16):
-        kc = rng.integers(0, 8 if preset == oracle.K3V4_NC else 256, 128).astype(np.uint8)
+        kc = rng.integers(0, KEY_CODES[preset], 128).astype(np.uint8)
         vc = rng.integers(0, 16, 128).astype(np.uint8)
         m = [int(x) for x in rng.integers(0, 65536, 4)]
         if preset == oracle.K8V4:
@@ -195,8 +271,10 @@ def test_record_round_trip_and_slot_size(preset):
     seen = np.zeros(block.size, np.int32)
     for tb in range(16):
         b2 = np.zeros_like(block)
-        oracle.write_record(preset, b2, tb, np.full(128, 7 if preset == oracle.K3V4_NC else 255, np.uint8),
-                            np.full(128, 15, np.uint8), 0xFFFF, 0xFFFF if preset == oracle.K3V4_NC else 0,
+        # (k4: code 0 is the nibble 15, every key bit set)
+        full = {oracle.K8V4: 255, oracle.K3V4_NC: 7, oracle.K4V4_NC: 0}[preset]
+        oracle.write_record(preset, b2, tb, np.full(128, full, np.uint8),
+                            np.full(128, 15, np.uint8), 0xFFFF, 0 if preset == oracle.K8V4 else 0xFFFF,
                             0xFFFF, 0xFFFF)
         seen += (b2 != 0)
     assert np.all(seen == 1)
@@ -205,7 +283,7 @@ def test_record_round_trip_and_slot_size(preset):
 def test_store_writes_the_quantised_record():
     from tests import synth
     rng = np.random.default_rng(27)
-    for preset in (oracle.K8V4, oracle.K3V4_NC):
+    for preset in (oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC):
         B, Hk, S = 2, 2, 40
         cache = np.zeros(oracle.cache_bytes(preset, B, Hk, S), np.uint8)
         K = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
@@ -217,8 +295,9 @@ def test_store_writes_the_quantised_record():
         for (b, s, hk) in [(0, 0, 0), (1, 39, 1), (0, 17, 1), (1, 16, 0)]:
             blk = cache[((b * Hk + hk) * nblk + s // 16) * bb:][:bb]
             kc, vc, m0, m1, vs, vz = oracle.read_record(preset, blk, s % 16)
-            if preset == oracle.K3V4_NC:
-                c2, n2, g2 = oracle.quant_key_k3(K[b, s, hk])
+            if preset != oracle.K8V4:
+                quant = oracle.quant_key_k3 if preset == oracle.K3V4_NC else oracle.quant_key_k4
+                c2, n2, g2 = quant(K[b, s, hk])
                 assert (m0, m1) == (n2, g2)
             else:
                 c2, s2 = oracle.quant_key_k8(K[b, s, hk])

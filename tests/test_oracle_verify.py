@@ -39,7 +39,7 @@ def _sdpa_reference(preset, cache, B, Hk, max_seq, Q, seq_lens, Hq, causal):
             for g in range(G):
                 hq = hk * G + g
                 q = Q[:, b, hq].astype(np.float64)
-                if preset == oracle.K3V4_NC:
+                if preset != oracle.K8V4:
                     q = q @ H.T
                 mask = torch.ones(N, L, dtype=torch.bool)
                 if causal:
@@ -52,7 +52,7 @@ def _sdpa_reference(preset, cache, B, Hk, max_seq, Q, seq_lens, Hq, causal):
     return out
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 @pytest.mark.parametrize("causal", [True, False])
 def test_verify_matches_torch_sdpa_float64(preset, causal):
     rng = np.random.default_rng(31)
@@ -79,7 +79,7 @@ def test_fp16_query_path():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 def test_zero_query_gives_mean_of_values(preset):
     """All scores equal -> uniform softmax -> mean of the dequantised values."""
     rng = np.random.default_rng(33)
@@ -108,7 +108,7 @@ def test_dominant_score_selects_one_value():
     assert np.allclose(out[0, 0, 0], v5, atol=1e-12)
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 def test_causal_special_cases_and_looped_equivalence(preset):
     rng = np.random.default_rng(35)
     N, B, Hq, Hk, S = 5, 2, 4, 1, 30
@@ -131,7 +131,7 @@ def test_causal_special_cases_and_looped_equivalence(preset):
     assert np.array_equal(d1, d2)
 
 
-@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC])
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
 def test_causality_invariance(preset):
     """Changing K/V at positions a row may not see leaves that row bit-identical."""
     rng = np.random.default_rng(36)
@@ -175,7 +175,7 @@ def test_quantised_attention_close_to_exact_attention():
     sl = np.array([S], np.int32)
     Kt = torch.tensor(K[0, :, 0].astype(np.float64))
     errs = {}
-    for preset, tol in ((oracle.K8V4, 0.05), (oracle.K3V4_NC, 0.25)):
+    for preset, tol in ((oracle.K8V4, 0.05), (oracle.K3V4_NC, 0.25), (oracle.K4V4_NC, 0.14)):
         cache = _build(preset, B, Hk, S, K, V)
         Vh = torch.tensor(np.stack([oracle.dequant(preset, cache, Hk, S, 0, 0, t)[1] for t in range(S)]))
         got = oracle.verify(preset, cache, B, Hk, S, Q, sl, Hq, False)
