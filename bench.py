@@ -293,7 +293,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "%s: preset=%s N_spec=%d B=%d Hq=%d Hk=%d D=128 seqlen=%d causal=%s"
-                        % (args.workload, "k8v4" if preset == 1 else "k3v4_nc", N, B, Hq, Hk, S,
+                        % (args.workload, {1: "k8v4", 2: "k3v4_nc", 3: "k4v4_nc"}[preset], N, B, Hq, Hk, S,
                            cfg["causal"]),
             "num_splits": splits,
             "cold_replicas": R,

@@ -7,7 +7,8 @@
  * 2026-04-14):
  *   - tqkv_store  is the fused store (Context section: Walsh-Hadamard
  *     rotation + Lloyd-Max codebook for keys, uniform scalar quantisation for
- *     values; the k8v4 preset keeps FP8 keys, Part 6);
+ *     values, 3-4 bits per coordinate; the k8v4 preset keeps FP8 keys,
+ *     Part 6);
  *   - tqkv_verify is the fused N_spec verification attention of Part 3
  *     (query [N_spec, B, Hq, D] -> output of the same shape) with the causal
  *     window of Part 4 (query n attends to cached_len + n + 1 tokens) and the
@@ -34,9 +35,10 @@
  *   base + ((b * Hk + hk) * nblk + blk) * tqkv_block_bytes(preset),
  * nblk = ceil(max_seq / 16).  A k3v4_nc block is 1920 B (120 B per token:
  * 48 B of 3-bit key codes, 64 B of 4-bit value codes, fp16 norm, fp16 norm
- * correction, fp16 value scale, fp16 value zero); a k8v4 block is 3168 B
- * (198 B per token: 128 B of FP8 E4M3 key codes, 64 B of value codes, fp16
- * key scale, value scale, value zero).  The exact byte and bit placement is
+ * correction, fp16 value scale, fp16 value zero); a k4v4_nc block is 2176 B
+ * (136 B per token: 64 B of 4-bit key codes, then the same fields as
+ * k3v4_nc); a k8v4 block is 3168 B (198 B per token: 128 B of FP8 E4M3 key
+ * codes, 64 B of value codes, fp16 key scale, value scale, value zero).  The exact byte and bit placement is
  * given by the byte offsets in the library source (common.h); the stored
  * bytes of a token depend only on that token's K and V.
  *
@@ -68,7 +70,8 @@ extern "C" {
 
 typedef enum {
     TQKV_K8V4 = 1,    /* FP8 E4M3 keys with a per-token fp16 scale, 4-bit values */
-    TQKV_K3V4_NC = 2  /* WHT-rotated 3-bit Lloyd-Max keys + norm correction, 4-bit values */
+    TQKV_K3V4_NC = 2, /* WHT-rotated 3-bit Lloyd-Max keys + norm correction, 4-bit values */
+    TQKV_K4V4_NC = 3  /* the same with 4-bit (16-level) Lloyd-Max keys */
 } tqkv_preset;
 
 typedef enum {
@@ -115,7 +118,8 @@ typedef struct tqkv_paged_cache {
                                    16 * max_pages per sequence, <= TQKV_MAX_PAGES_PER_SEQ */
 } tqkv_paged_cache;
 
-/* Bytes per token and KV head: 120 (k3v4_nc) or 198 (k8v4); 0 for a bad preset. */
+/* Bytes per token and KV head: 120 (k3v4_nc), 136 (k4v4_nc) or 198 (k8v4);
+ * 0 for a bad preset. */
 size_t tqkv_slot_bytes(int preset);
 
 /* Bytes per 16-token block: 16 * tqkv_slot_bytes(preset). */
@@ -132,9 +136,10 @@ size_t tqkv_paged_cache_bytes(int preset, int Hk, int D, int num_pages);
  *   K, V     device, fp16 [T, Hk, 128] (row-major), 2-byte aligned
  *   seq_idx  device, int32 [T]: sequence of token t, in [0, B)
  *   pos      device, int32 [T]: position of token t, in [0, max_seq)
- * Keys (k3v4_nc): fp32 norm n, normalised Sylvester WHT of k/n, 3-bit code
- * per coordinate against the N(0, 1/128) Lloyd-Max thresholds, norm
- * correction gamma = 1/||c[codes]||, fp16 n and gamma.  Keys (k8v4): scale
+ * Keys (k3v4_nc, k4v4_nc): fp32 norm n, normalised Sylvester WHT of k/n, a
+ * 3-bit (4-bit) code per coordinate against the 8 (16) N(0, 1/128)
+ * Lloyd-Max levels, norm correction gamma = 1/||c[codes]||, fp16 n and
+ * gamma.  Keys (k8v4): scale
  * s = fp16(max|k| / 448), codes = e4m3(k / s) rounded to nearest even and
  * saturated.  Values: zero = min v, scale = fp16((max v - min v) / 15),
  * code = clamp(rint((v - zero) / scale), 0, 15).  The bytes written are
@@ -179,8 +184,8 @@ int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int
  *   workspace device, 256-byte aligned, >= tqkv_verify_workspace_bytes(...)
  *             (may be NULL when that is 0); its contents on entry do not
  *             matter and are overwritten
- * Query head hq reads KV head hq / (Hq / Hk).  k3v4_nc queries are rotated by
- * the same normalised WHT as the keys.  Preconditions (device values):
+ * Query head hq reads KV head hq / (Hq / Hk).  k3v4_nc and k4v4_nc queries
+ * are rotated by the same normalised WHT as the keys.  Preconditions (device values):
  * n_spec <= seq_lens[b] <= max_seq and every token below seq_lens[b] was
  * stored; a larger seq_lens[b] is clamped to max_seq, and a row that sees no
  * token is NaN.  The result matches plain softmax attention over the

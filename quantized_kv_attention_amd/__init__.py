@@ -36,7 +36,7 @@ import os
 import torch
 
 __all__ = [
-    "K8V4", "K3V4_NC", "HEAD_DIM", "BLOCK_TOKENS", "MAX_QLEN", "TqkvError", "Cache", "PagedCache",
+    "K8V4", "K3V4_NC", "K4V4_NC", "HEAD_DIM", "BLOCK_TOKENS", "MAX_QLEN", "TqkvError", "Cache", "PagedCache",
     "library_path", "tqkv_slot_bytes", "tqkv_block_bytes", "tqkv_cache_bytes", "tqkv_store",
     "tqkv_verify_num_splits", "tqkv_verify_workspace_bytes", "tqkv_verify", "tqkv_store_verify",
     "tqkv_verify_varlen", "tqkv_paged_cache_bytes", "tqkv_paged_store", "tqkv_paged_verify_num_splits",
@@ -46,6 +46,7 @@ __all__ = [
 
 K8V4 = 1
 K3V4_NC = 2
+K4V4_NC = 3
 HEAD_DIM = 128
 BLOCK_TOKENS = 16
 MAX_QLEN = 128

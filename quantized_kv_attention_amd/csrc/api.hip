@@ -45,20 +45,18 @@ struct View {
 
 int nblocks(int max_seq) { return (max_seq + kBlockTokens - 1) / kBlockTokens; }
 
-int check_preset(int preset, int D)
-{
-    if (preset != TQKV_K8V4 && preset != TQKV_K3V4_NC)
-        return TQKV_ERR_ARG;
-    if (D != TQKV_HEAD_DIM)
-        return TQKV_ERR_UNSUPPORTED;
-    return TQKV_OK;
-}
+bool known_preset(int preset) { return preset == TQKV_K8V4 || preset == TQKV_K3V4_NC || preset == TQKV_K4V4_NC; }
+static_assert(TQKV_K8V4 == kPresetK8V4 && TQKV_K3V4_NC == kPresetK3V4 && TQKV_K4V4_NC == kPresetK4V4, "preset ids");
+static_assert(Layout<kPresetK8V4>::kBlockBytes == 16 * 198 && Layout<kPresetK3V4>::kBlockBytes == 16 * 120 &&
+                  Layout<kPresetK4V4>::kBlockBytes == 16 * 136,
+              "block bytes");
+
 
 int view_of(const tqkv_cache *c, View &v)
 {
     if (!c)
         return TQKV_ERR_ARG;
-    if (c->preset != TQKV_K8V4 && c->preset != TQKV_K3V4_NC)
+    if (!known_preset(c->preset))
         return TQKV_ERR_ARG;
     if (c->B < 1 || c->Hk < 1 || c->max_seq < 1 || !c->base)
         return TQKV_ERR_ARG;
@@ -75,7 +73,7 @@ int check_pool(const tqkv_paged_cache *c)
 {
     if (!c)
         return TQKV_ERR_ARG;
-    if (c->preset != TQKV_K8V4 && c->preset != TQKV_K3V4_NC)
+    if (!known_preset(c->preset))
         return TQKV_ERR_ARG;
     if (c->Hk < 1 || c->num_pages < 1 || c->num_pages > (INT32_MAX >> 4) || !c->base)
         return TQKV_ERR_ARG;
@@ -353,6 +351,8 @@ size_t tqkv_slot_bytes(int preset)
 {
     if (preset == TQKV_K3V4_NC)
         return 120;
+    if (preset == TQKV_K4V4_NC)
+        return 136;
     if (preset == TQKV_K8V4)
         return 198;
     return 0;
@@ -529,6 +529,6 @@ const char *tqkv_status_string(int status)
     }
 }
 
-int tqkv_version(void) { return 110; }
+int tqkv_version(void) { return 200; }
 
 } // extern "C"

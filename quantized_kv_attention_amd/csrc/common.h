@@ -11,10 +11,16 @@ constexpr int kD = 128;
 constexpr int kBlockTokens = 16;
 constexpr int kPresetK8V4 = 1;
 constexpr int kPresetK3V4 = 2;
+constexpr int kPresetK4V4 = 3;
+// Lloyd-Max key presets: WHT-rotated keys, codes against the 8- or 16-level
+// codebook, fp16 norm and norm-correction fields
+template <int P> constexpr bool kLloydMax = (P == kPresetK3V4 || P == kPresetK4V4);
 
 // Byte layout of one 16-token block (see include/tqkv.h for the overview).
 //   k3v4_nc: key codes [0,768) 48 B/token | value nibbles [768,1792) |
 //            n_h[16] @1792 | gamma_h[16] @1824 | vscale[16] @1856 | vzero[16] @1888
+//   k4v4_nc: key nibbles [0,1024) 64 B/token | value nibbles [1024,2048) |
+//            n_h[16] @2048 | gamma_h[16] @2080 | vscale[16] @2112 | vzero[16] @2144
 //   k8v4:    e4m3 keys [0,2048) 128 B/token | value nibbles [2048,3072) |
 //            kscale[16] @3072 | vscale[16] @3104 | vzero[16] @3136
 template <int P> struct Layout;
@@ -26,6 +32,15 @@ template <> struct Layout<kPresetK3V4> {
     static constexpr int kMeta1 = 1824; // gamma_h
     static constexpr int kVScale = 1856;
     static constexpr int kVZero = 1888;
+};
+template <> struct Layout<kPresetK4V4> {
+    static constexpr int kBlockBytes = 2176;
+    static constexpr int kKeyBytesPerToken = 64;
+    static constexpr int kValOff = 1024;
+    static constexpr int kMeta0 = 2048; // n_h
+    static constexpr int kMeta1 = 2080; // gamma_h
+    static constexpr int kVScale = 2112;
+    static constexpr int kVZero = 2144;
 };
 template <> struct Layout<kPresetK8V4> {
     static constexpr int kBlockBytes = 3168;

@@ -4,8 +4,9 @@
 // Method (Context and Part 6 of "Speculative decoding on Intel Arc:
 // TurboQuant KV + a fused N_spec kernel"): keys are rotated by a
 // Walsh-Hadamard transform and coded with a precomputed Lloyd-Max codebook
-// plus a norm correction (k3v4_nc), or kept as FP8 E4M3 codes (k8v4); values
-// get uniform 4-bit codes with a scale and a zero.
+// plus a norm correction (k3v4_nc with 8 levels, k4v4_nc with 16: the
+// method's 3-4 bits per coordinate, TL;DR), or kept as FP8 E4M3 codes (k8v4);
+// values get uniform 4-bit codes with a scale and a zero.
 //
 // One wavefront quantises one token-head (128 coordinates): lane l holds
 // coordinates l and l + 64, so the last WHT stage and the first step of the
@@ -54,6 +55,29 @@ __device__ inline int lloyd_code(float y)
         c += (y >= kThreshold[j]) ? 1 : 0; // NaN compares false: code 0
     return c;
 }
+
+// 16 levels: |c16_c| through the symmetry c16_(15-j) = -c16_j (the sign
+// does not enter the norm correction), and the code from 15 thresholds
+__device__ inline float centroid16_abs(int c)
+{
+    const int m = (c >= 8) ? c - 8 : 7 - c; // rank of |c16_c| from zero
+    float lo = (m & 2) ? ((m & 1) ? kCentroid16[11] : kCentroid16[10]) : ((m & 1) ? kCentroid16[9] : kCentroid16[8]);
+    float hi = (m & 2) ? ((m & 1) ? kCentroid16[15] : kCentroid16[14]) : ((m & 1) ? kCentroid16[13] : kCentroid16[12]);
+    return (m & 4) ? hi : lo;
+}
+
+__device__ inline int lloyd_code16(float y)
+{
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 15; ++j)
+        c += (y >= kThreshold16[j]) ? 1 : 0; // NaN compares false: code 0
+    return c;
+}
+
+// Stored k4v4_nc key nibble of code c: sign-magnitude, bit 3 set for the
+// negative levels (c < 8), bits 0-2 the rank of |c16_c| from zero.
+__device__ inline uint32_t k4_nibble(int c) { return (uint32_t)((c >= 8) ? c - 8 : 15 - c); }
 
 // x from lane (lane ^ S) of the wavefront, S = 1, 2, ..., 32, without the
 // LDS crossbar: DPP moves within rows of 16 lanes (xor 1, 2: quad
@@ -147,14 +171,15 @@ __device__ inline TokenHead load_token_head(const uint16_t *kp, const uint16_t *
 }
 
 // The quantised record of one token-head, as this lane holds it before the
-// stores: 3-bit key code words (k3v4_nc) or this lane's two FP8 codes
-// (k8v4), the key metadata, this lane's value byte and the value scale /
-// zero.  Splitting computation from stores lets two token-heads' dependent
-// exchange chains run interleaved.
+// stores: 3-bit key code words (k3v4_nc), two key nibble dwords (k4v4_nc)
+// or this lane's two FP8 codes (k8v4), the key metadata, this lane's value
+// byte and the value scale / zero.  Splitting computation from stores lets
+// two token-heads' dependent exchange chains run interleaved.
 struct Record {
-    uint32_t kw[2][3];  // k3v4_nc: the key code words of this lane's triple (both halves)
+    uint32_t kw[2][3];  // k3v4_nc: the key code words of this lane's triple (both halves);
+                        // k4v4_nc: kw[hh][0] = key dword 8hh + lane / 8
     uint32_t c0, c1;    // k8v4: FP8 codes of coordinates lane, lane + 64
-    uint16_t m0, m1;    // k3v4_nc: n, gamma; k8v4: key scale
+    uint16_t m0, m1;    // k3v4_nc, k4v4_nc: n, gamma; k8v4: key scale
     uint16_t sch, zh;   // value scale, zero
     uint32_t vbyte;     // this lane's value nibble byte
     int vpos;           // ... and its byte index p (coordinates 2p, 2p + 1)
@@ -168,7 +193,7 @@ __device__ inline Record quantize_record(const TokenHead &in, int lane)
     Record r;
     // ---------------------------------------------------------------- keys
     float x0 = h2f_q(in.k0), x1 = h2f_q(in.k1);
-    if constexpr (PRESET == kPresetK3V4) {
+    if constexpr (kLloydMax<PRESET>) {
         const float n = sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(x0, x0), __fmul_rn(x1, x1)), lane));
 #pragma unroll
         for (int h = 1; h < 64; h <<= 1) {
@@ -187,47 +212,73 @@ __device__ inline Record quantize_record(const TokenHead &in, int lane)
             x1 = __fsub_rn(u, v);
         }
         const float rr = __fdiv_rn(1.0f, __fmul_rn(sqrt_rn(128.0f), n));
-        const int c0 = lloyd_code(__fmul_rn(x0, rr));
-        const int c1 = lloyd_code(__fmul_rn(x1, rr));
-        const float q0 = centroid(c0), q1 = centroid(c1);
+        const float y0 = __fmul_rn(x0, rr), y1 = __fmul_rn(x1, rr);
+        int c0, c1;
+        float q0, q1;
+        if constexpr (PRESET == kPresetK3V4) {
+            c0 = lloyd_code(y0);
+            c1 = lloyd_code(y1);
+            q0 = centroid(c0);
+            q1 = centroid(c1);
+        } else {
+            c0 = lloyd_code16(y0);
+            c1 = lloyd_code16(y1);
+            q0 = centroid16_abs(c0);
+            q1 = centroid16_abs(c1);
+        }
         const float gam = __fdiv_rn(1.0f, sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(q0, q0), __fmul_rn(q1, q1)), lane)));
-
-        // Bit placement: coordinate d = 64h + 32g + 8k + e -> dword triple
-        // 6h+3g+{0,1,2}, byte lane e%4, slot 2k + e/4.  Slots 0-5 hold all
-        // three bits at word slot/2, offset 3*(slot%2); slots 6 and 7 keep
-        // bits 0-1 at offset 6 of word slot-6 and bit 2 at offset slot of
-        // word 2.  Lane l carries d = l (h = 0) and d = l + 64 (h = 1), both
-        // in triple g = l/32 of their half.
-        uint32_t w[2][3] = {{0, 0, 0}, {0, 0, 0}};
-        {
-            const int k = (lane >> 3) & 3, e = lane & 7;
-            const int sl = 2 * k + (e >> 2), sh = 8 * (e & 3);
-            const uint32_t cc[2] = {(uint32_t)c0, (uint32_t)c1};
+        r.m0 = f2h(n);
+        r.m1 = f2h(gam);
+        r.c0 = r.c1 = 0u;
+        if constexpr (PRESET == kPresetK4V4) {
+            // coordinate d = 8j + e -> key dword j, byte e % 4, nibble e / 4;
+            // lane l carries d = l (dword l / 8) and d = l + 64 (dword 8 +
+            // l / 8); the 8 lanes of a dword OR their nibbles together
+            const int sh = 8 * (lane & 3) + 4 * ((lane >> 2) & 1);
+            uint32_t w0 = k4_nibble(c0) << sh, w1 = k4_nibble(c1) << sh;
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                if (sl < 6) {
-                    w[hh][sl >> 1] |= cc[hh] << (sh + 3 * (sl & 1));
-                } else {
-                    w[hh][sl - 6] |= (cc[hh] & 3u) << (sh + 6);
-                    w[hh][2] |= (cc[hh] >> 2) << (sh + sl);
+            for (int s = 1; s < 8; s <<= 1) {
+                w0 |= lane_xor_n(w0, s, lane);
+                w1 |= lane_xor_n(w1, s, lane);
+            }
+            r.kw[0][0] = w0;
+            r.kw[1][0] = w1;
+            r.kw[0][1] = r.kw[0][2] = r.kw[1][1] = r.kw[1][2] = 0u;
+        } else {
+            // Bit placement: coordinate d = 64h + 32g + 8k + e -> dword triple
+            // 6h+3g+{0,1,2}, byte lane e%4, slot 2k + e/4.  Slots 0-5 hold all
+            // three bits at word slot/2, offset 3*(slot%2); slots 6 and 7 keep
+            // bits 0-1 at offset 6 of word slot-6 and bit 2 at offset slot of
+            // word 2.  Lane l carries d = l (h = 0) and d = l + 64 (h = 1), both
+            // in triple g = l/32 of their half.
+            uint32_t w[2][3] = {{0, 0, 0}, {0, 0, 0}};
+            {
+                const int k = (lane >> 3) & 3, e = lane & 7;
+                const int sl = 2 * k + (e >> 2), sh = 8 * (e & 3);
+                const uint32_t cc[2] = {(uint32_t)c0, (uint32_t)c1};
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    if (sl < 6) {
+                        w[hh][sl >> 1] |= cc[hh] << (sh + 3 * (sl & 1));
+                    } else {
+                        w[hh][sl - 6] |= (cc[hh] & 3u) << (sh + 6);
+                        w[hh][2] |= (cc[hh] >> 2) << (sh + sl);
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int s = 1; s < 32; s <<= 1)
+            for (int s = 1; s < 32; s <<= 1)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int j = 0; j < 3; ++j)
+                        w[hh][j] |= lane_xor_n(w[hh][j], s, lane);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int j = 0; j < 3; ++j)
-                    w[hh][j] |= lane_xor_n(w[hh][j], s, lane);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                r.kw[hh][j] = w[hh][j];
-        r.m0 = f2h(n);
-        r.m1 = f2h(gam);
-        r.c0 = r.c1 = 0u;
+                    r.kw[hh][j] = w[hh][j];
+        }
     } else {
         float amax = fmaxf(fmaxf(0.0f, fabsf(x0)), fabsf(x1));
 #pragma unroll
@@ -285,6 +336,16 @@ __device__ inline void store_record(uint8_t *blk, int tb, const Record &r, int l
                 kd[3 * g + j] = r.kw[0][j];
                 kd[6 + 3 * g + j] = r.kw[1][j];
             }
+        }
+        if (lane == 0)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = r.m0;
+        if (lane == 1)
+            *reinterpret_cast<uint16_t *>(blk + L::kMeta1 + 2 * tb) = r.m1;
+    } else if constexpr (PRESET == kPresetK4V4) {
+        if ((lane & 7) == 0) {
+            uint32_t *kd = reinterpret_cast<uint32_t *>(blk + tb * L::kKeyBytesPerToken);
+            kd[lane >> 3] = r.kw[0][0];
+            kd[8 + (lane >> 3)] = r.kw[1][0];
         }
         if (lane == 0)
             *reinterpret_cast<uint16_t *>(blk + L::kMeta0 + 2 * tb) = r.m0;

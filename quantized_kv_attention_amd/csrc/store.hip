@@ -64,6 +64,8 @@ hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s)
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     if (preset == kPresetK3V4)
         hipLaunchKernelGGL(store_kernel<kPresetK3V4>, grid, block, 0, s, a);
+    else if (preset == kPresetK4V4)
+        hipLaunchKernelGGL(store_kernel<kPresetK4V4>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(store_kernel<kPresetK8V4>, grid, block, 0, s, a);
     return hipGetLastError();

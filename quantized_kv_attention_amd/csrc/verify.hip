@@ -81,6 +81,10 @@ template <int NQT> struct Ring<kPresetK3V4, NQT> {
     static constexpr int kLoads = 4; // ceil(2 * 1920 / 1024)
     static constexpr int kDepth = 4 * NQT;
 };
+template <int NQT> struct Ring<kPresetK4V4, NQT> {
+    static constexpr int kLoads = 5; // ceil(2 * 2176 / 1024)
+    static constexpr int kDepth = 3 * NQT;
+};
 template <int NQT> struct Ring<kPresetK8V4, NQT> {
     static constexpr int kLoads = 7; // ceil(2 * 3168 / 1024)
     static constexpr int kDepth = 2 * NQT;
@@ -230,6 +234,10 @@ template <> struct KeyRegs<kPresetK3V4> {
     uint2 k[3];      // 24 B: this lane's 64 key codes (two 32-code dword triples)
     uint32_t tab[4]; // byte tables of the 8 centroids times n*gamma: lo 0-3, lo 4-7, hi 0-3, hi 4-7
 };
+template <> struct KeyRegs<kPresetK4V4> {
+    u32x4 k[2];      // 32 B: this lane's 64 key nibbles (one dword per 8 coordinates)
+    uint32_t tab[4]; // byte tables of the 8 level magnitudes times n*gamma: lo 0-3, lo 4-7, hi 0-3, hi 4-7
+};
 template <> struct KeyRegs<kPresetK8V4> {
     u32x4 k[4];  // 64 B: this lane's 64 e4m3 key codes
     uint32_t kf; // the token's key scale (fp16) in both halves
@@ -256,9 +264,10 @@ __device__ inline uint32_t hmul2(uint32_t a, uint32_t b)
 // The lane's key codes and key factor.  The factor (the per-token key scale,
 // or n * gamma) multiplies the key operand instead of the score column: for
 // FP8 with one packed fp16 multiply per code pair (the scale operand of
-// v_cvt_scalef32_pk_f16_fp8 only applies a power of two), for the 3-bit
-// codes through a per-lane table of scaled centroids (4 multiplies + 4 byte
-// permutes per tile).
+// v_cvt_scalef32_pk_f16_fp8 only applies a power of two), for the 3- and
+// 4-bit codes through a per-lane table of 8 scaled levels (4 multiplies + 4
+// byte permutes per tile; the 16-level codebook is symmetric, so its table
+// holds the magnitudes and the code's sign bit becomes the fp16 sign).
 template <int PRESET>
 __device__ inline void read_keys(KeyRegs<PRESET> &t, const uint8_t *slot, int lane)
 {
@@ -279,6 +288,23 @@ __device__ inline void read_keys(KeyRegs<PRESET> &t, const uint8_t *slot, int la
         const uint32_t c23 = hmul2(kCentroidHalf[2] | ((uint32_t)kCentroidHalf[3] << 16), ff);
         const uint32_t c45 = hmul2(kCentroidHalf[4] | ((uint32_t)kCentroidHalf[5] << 16), ff);
         const uint32_t c67 = hmul2(kCentroidHalf[6] | ((uint32_t)kCentroidHalf[7] << 16), ff);
+        t.tab[0] = perm(c23, c01, 0x06040200u);
+        t.tab[1] = perm(c67, c45, 0x06040200u);
+        t.tab[2] = perm(c23, c01, 0x07050301u);
+        t.tab[3] = perm(c67, c45, 0x07050301u);
+    } else if constexpr (PRESET == kPresetK4V4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            t.k[j] = *reinterpret_cast<const u32x4 *>(kb + 32 * h + 16 * j);
+        const uint32_t n = *reinterpret_cast<const uint16_t *>(blk + L::kMeta0 + 2 * (tok & 15));
+        const uint32_t g = *reinterpret_cast<const uint16_t *>(blk + L::kMeta1 + 2 * (tok & 15));
+        const uint32_t f = hmul2(n, g);
+        const uint32_t ff = f | (f << 16);
+        // magnitudes: levels 8..15 of the ascending codebook
+        const uint32_t c01 = hmul2(kCentroidHalf16[8] | ((uint32_t)kCentroidHalf16[9] << 16), ff);
+        const uint32_t c23 = hmul2(kCentroidHalf16[10] | ((uint32_t)kCentroidHalf16[11] << 16), ff);
+        const uint32_t c45 = hmul2(kCentroidHalf16[12] | ((uint32_t)kCentroidHalf16[13] << 16), ff);
+        const uint32_t c67 = hmul2(kCentroidHalf16[14] | ((uint32_t)kCentroidHalf16[15] << 16), ff);
         t.tab[0] = perm(c23, c01, 0x06040200u);
         t.tab[1] = perm(c67, c45, 0x06040200u);
         t.tab[2] = perm(c23, c01, 0x07050301u);
@@ -343,6 +369,19 @@ __device__ inline half8_t key_operand(const KeyRegs<PRESET> &t, int ks)
         }
         k3_lookup(t.tab, sa, o.u[0], o.u[1]);
         k3_lookup(t.tab, sb, o.u[2], o.u[3]);
+    } else if constexpr (PRESET == kPresetK4V4) {
+        // dword ks of the lane's eight: byte b holds coordinate b (low
+        // nibble) and b + 4 (high nibble); nibble bits 0-2 index the
+        // magnitude table, bit 3 is the sign
+        const uint32_t d = t.k[ks >> 2][ks & 3];
+        const uint32_t ia = d & 0x07070707u, ib = (d >> 4) & 0x07070707u;
+        const uint32_t la = perm(t.tab[1], t.tab[0], ia), lb = perm(t.tab[1], t.tab[0], ib);
+        const uint32_t ha = perm(t.tab[3], t.tab[2], ia) | ((d << 4) & 0x80808080u);
+        const uint32_t hb = perm(t.tab[3], t.tab[2], ib) | (d & 0x80808080u);
+        o.u[0] = perm(ha, la, 0x05010400u);
+        o.u[1] = perm(ha, la, 0x07030602u);
+        o.u[2] = perm(hb, lb, 0x05010400u);
+        o.u[3] = perm(hb, lb, 0x07030602u);
     } else {
         const uint32_t a = t.k[ks >> 1][2 * (ks & 1)], b = t.k[ks >> 1][2 * (ks & 1) + 1];
         const half2_t f = __builtin_bit_cast(half2_t, t.kf);
@@ -740,10 +779,10 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         lds_barrier();
     }
 
-    // 6. k3v4_nc: rotate by the normalised WHT, q' = H q / sqrt(128), as the
-    //    MFMA product Q'^T = H Q^T; wavefront w computes output coordinates
-    //    32w..32w+31 of every row and writes them back in place
-    if constexpr (PRESET == kPresetK3V4) {
+    // 6. Lloyd-Max keys: rotate by the normalised WHT, q' = H q / sqrt(128),
+    //    as the MFMA product Q'^T = H Q^T; wavefront w computes output
+    //    coordinates 32w..32w+31 of every row and writes them back in place
+    if constexpr (kLloydMax<PRESET>) {
         half8_t Bq[NQT][8];
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
@@ -1402,6 +1441,11 @@ void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t
             hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, true, TR>), grid, block, 0, s, a);
         else
             hipLaunchKernelGGL((verify_kernel<kPresetK3V4, NQT, false, TR>), grid, block, 0, s, a);
+    } else if (preset == kPresetK4V4) {
+        if (paged)
+            hipLaunchKernelGGL((verify_kernel<kPresetK4V4, NQT, true, TR>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((verify_kernel<kPresetK4V4, NQT, false, TR>), grid, block, 0, s, a);
     } else {
         if (paged)
             hipLaunchKernelGGL((verify_kernel<kPresetK8V4, NQT, true, TR>), grid, block, 0, s, a);

@@ -14,6 +14,7 @@ and a long-context step):
   tiny_k8v4        N=8 B=1  Hq=8  Hk=1 S=512    causal, Q/K/V fp16, seed 0
   poc_k8v4         N=8 B=4  Hq=32 Hk=4 S=8192   causal, Q fp32,     seed 1
   poc_k3v4_nc      same shape and inputs as poc_k8v4,                 seed 1
+  poc_k4v4_nc      same shape and inputs as poc_k8v4,                 seed 1
   decode_k3v4_nc   N=1 B=32 Hq=32 Hk=8 S=32768  non-causal, Q fp32,   seed 3
   long_k3v4_nc     N=8 B=1  Hq=32 Hk=4 S=262144 causal, Q fp32,       seed 4
 Held-out parity seeds: 101, 202, 303, 404, 505.
@@ -24,6 +25,7 @@ import numpy as np
 
 K8V4 = 1
 K3V4_NC = 2
+K4V4_NC = 3
 D = 128
 
 HELD_OUT_SEEDS = (101, 202, 303, 404, 505)
@@ -34,6 +36,8 @@ CONFIGS = {
     "poc_k8v4": dict(preset=K8V4, N=8, B=4, Hq=32, Hk=4, S=8192, causal=True,
                      q_dtype=np.float32, seed=1),
     "poc_k3v4_nc": dict(preset=K3V4_NC, N=8, B=4, Hq=32, Hk=4, S=8192, causal=True,
+                        q_dtype=np.float32, seed=1),
+    "poc_k4v4_nc": dict(preset=K4V4_NC, N=8, B=4, Hq=32, Hk=4, S=8192, causal=True,
                         q_dtype=np.float32, seed=1),
     "decode_k3v4_nc": dict(preset=K3V4_NC, N=1, B=32, Hq=32, Hk=8, S=32768, causal=False,
                            q_dtype=np.float32, seed=3),

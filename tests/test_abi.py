@@ -33,9 +33,12 @@ def test_binding_names_match_header():
 
 def test_sizes():
     assert tq.tqkv_slot_bytes(tq.K3V4_NC) == 120
+    assert tq.tqkv_slot_bytes(tq.K4V4_NC) == 136
     assert tq.tqkv_slot_bytes(tq.K8V4) == 198
     assert tq.tqkv_slot_bytes(7) == 0
+    assert tq.tqkv_slot_bytes(0) == 0
     assert tq.tqkv_block_bytes(tq.K3V4_NC) == 1920
+    assert tq.tqkv_block_bytes(tq.K4V4_NC) == 2176
     assert tq.tqkv_block_bytes(tq.K8V4) == 3168
     # PoC shape: B=4, Hk=4, 8192 tokens
     assert tq.tqkv_cache_bytes(tq.K3V4_NC, 4, 4, 128, 8192) == 4 * 4 * 8192 * 120
@@ -44,6 +47,24 @@ def test_sizes():
     assert tq.tqkv_cache_bytes(tq.K8V4, 1, 1, 64, 16) == 0
     assert tq.tqkv_cache_bytes(tq.K8V4, 0, 1, 128, 16) == 0
     assert tq.tqkv_version() >= 100
+
+
+def test_codebook_tables_match_oracle():
+    """The library's constant codebook tables (written by its own generator)
+    are, bit for bit, the oracle's binary32 levels and thresholds."""
+    import numpy as np
+
+    import oracle
+    src = open(os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", "codebook.h")).read()
+
+    def table(name):
+        body = re.search(r"\b%s\[\d+\] = \{([^}]*)\}" % name, src).group(1)
+        return np.array([float.fromhex(x.strip().rstrip("f")) for x in body.split(",")], np.float32)
+
+    for levels, cn, tn in ((8, "kCentroid", "kThreshold"), (16, "kCentroid16", "kThreshold16")):
+        c, t = oracle.codebook(levels)
+        assert table(cn).view(np.uint32).tolist() == c.view(np.uint32).tolist(), levels
+        assert table(tn).view(np.uint32).tolist() == t.view(np.uint32).tolist(), levels
 
 
 def _desc(**kw):
@@ -59,7 +80,7 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(preset=3), -1), (dict(B=0), -1), (dict(base=0), -1), (dict(D=64), -2),
+    (dict(preset=4), -1), (dict(preset=0), -1), (dict(B=0), -1), (dict(base=0), -1), (dict(D=64), -2),
     (dict(base=4100), -3),
 ])
 def test_store_rejects_bad_cache(kw, status):

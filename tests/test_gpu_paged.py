@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 
 tq = pytest.importorskip("quantized_kv_attention_amd")
 
-PRESETS = [synth.K8V4, synth.K3V4_NC]
-PNAME = {synth.K8V4: "k8v4", synth.K3V4_NC: "k3v4_nc"}
+PRESETS = [synth.K8V4, synth.K3V4_NC, synth.K4V4_NC]
+PNAME = {synth.K8V4: "k8v4", synth.K3V4_NC: "k3v4_nc", synth.K4V4_NC: "k4v4_nc"}
 
 
 def _kv(rng, B, S, Hk):

@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 
 tq = pytest.importorskip("quantized_kv_attention_amd")
 
-PRESETS = [synth.K8V4, synth.K3V4_NC]
-PNAME = {synth.K8V4: "k8v4", synth.K3V4_NC: "k3v4_nc"}
+PRESETS = [synth.K8V4, synth.K3V4_NC, synth.K4V4_NC]
+PNAME = {synth.K8V4: "k8v4", synth.K3V4_NC: "k3v4_nc", synth.K4V4_NC: "k4v4_nc"}
 
 
 def _small(preset, **kw):
@@ -59,7 +59,7 @@ def test_store_bit_exact_small(preset, seed):
     assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
 
 
-@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc"])
+@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc"])
 def test_store_bit_exact_config(name):
     cfg = synth.config(name)
     inp = synth.make_inputs(cfg)
@@ -142,7 +142,7 @@ def test_verify_shapes(preset, shape):
     assert_close(_gpu_verify(cache, cfg, inp), ref, what=str(shape))
 
 
-@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc"])
+@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc"])
 def test_verify_config_full(name):
     """Every output of the small configurations against the oracle, in the
     launch configuration the benchmark times (auto splits)."""
@@ -340,7 +340,7 @@ def test_verify_few_rows_nan_and_causality(preset):
 
 
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("name", ["poc_k8v4", "poc_k3v4_nc"])
+@pytest.mark.parametrize("name", ["poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc"])
 def test_step_config_full(name):
     """The steps the benchmark times, at the PoC shape, against the oracle:
     tqkv_store_verify (the N new tokens stored in the launch) and the paged
