@@ -34,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16 matrix peak
 PAGES_FUSED_TRITON_MS = {"poc_k8v4": 3.229, "poc_k3v4_nc": 4.83}  # Arc Pro B70, context
 
 
@@ -272,6 +273,9 @@ def main():
     qo_bytes = 2 * N * B * Hq * 128 * 4
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = (kv_bytes + qo_bytes) / (verify_ms * 1e-3) / 1e9
+    # the two fp16 contractions Q K^T and P V: 2 FLOPs per (row, token, d) each
+    flops = 4 * N * B * Hq * S * 128
+    tflops = flops / (verify_ms * 1e-3) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -321,6 +325,8 @@ def main():
             "bytes_per_launch": kv_bytes + qo_bytes,
             "measured_copy_GBps": round(copy_gbs, 1),
             "frac_of_measured_copy": round(achieved / copy_gbs, 4),
+            "mfma": {"flops_per_launch": flops, "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         },
         "cpu_baseline": cpu,
     }
