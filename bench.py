@@ -365,34 +365,46 @@ def cpu_baseline(cfg, seconds):
     preset = cfg["preset"]
     inp = synth.make_inputs(cfg)
     slot = oracle.slot_bytes(preset)
-    # sample: sequence 0 only (all of its KV heads), the whole sequence stored
-    # once outside the timing; the timed part is one step (store of the N new
+    # sample: the first nb sequences (all of their KV heads), as many as give
+    # every thread a (b, hk) unit -- the oracle's verify, the bulk of the
+    # step, runs one thread per unit; the sequences are stored once outside
+    # the timing, and the timed part is one step (store of their N new
     # tokens + verify), repeated until `seconds` have passed
-    cache = np.zeros(oracle.cache_bytes(preset, 1, Hk, S), np.uint8)
-    si, po = synth.token_lists(1, S)
-    oracle.store(preset, cache, 1, Hk, S, synth.rows(inp["K"][:1]), synth.rows(inp["V"][:1]), si, po)
-    si_n, po_n = synth.token_lists(1, S, S - N, S)
-    Kn = synth.rows(inp["K"][:1], S - N, S)
-    Vn = synth.rows(inp["V"][:1], S - N, S)
-    Q = np.ascontiguousarray(inp["Q"][:, :1])
-    sl = inp["seq_lens"][:1]
+    nb = min(B, max(1, threads // Hk))
+    cache = np.zeros(oracle.cache_bytes(preset, nb, Hk, S), np.uint8)
+    si, po = synth.token_lists(nb, S)
+    oracle.store(preset, cache, nb, Hk, S, synth.rows(inp["K"][:nb]), synth.rows(inp["V"][:nb]), si, po)
+    si_n, po_n = synth.token_lists(nb, S, S - N, S)
+    Kn = synth.rows(inp["K"][:nb], S - N, S)
+    Vn = synth.rows(inp["V"][:nb], S - N, S)
+    Q = np.ascontiguousarray(inp["Q"][:, :nb])
+    sl = inp["seq_lens"][:nb]
     reps, t_total = 0, 0.0
     while t_total < seconds or reps == 0:
         t0 = time.perf_counter()
-        oracle.store(preset, cache, 1, Hk, S, Kn, Vn, si_n, po_n)
-        oracle.verify(preset, cache, 1, Hk, S, Q, sl, Hq, cfg["causal"])
+        oracle.store(preset, cache, nb, Hk, S, Kn, Vn, si_n, po_n)
+        oracle.verify(preset, cache, nb, Hk, S, Q, sl, Hq, cfg["causal"])
         t_total += time.perf_counter() - t0
         reps += 1
     per_step = t_total / reps
-    kv = 1 * S * Hk * slot
+    kv = nb * S * Hk * slot
+    used = min(threads, nb * Hk)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(kv / per_step / 1e9, 4),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": used,
+        "threads_available": threads,
+        "cpu_model": model,
         "kind": "oracle",
-        "sample": "one of %d sequences (all %d KV heads, %d tokens, %d queries each): store of the "
+        "sample": "%d of %d sequences (all %d KV heads, %d tokens, %d queries each): store of the "
                   "%d new tokens + binary64 verify, %d reps, %.3f s per step" % (
-                      B, Hk, S, N * Hq, N, reps, per_step),
+                      nb, B, Hk, S, N * Hq, N, reps, per_step),
     }
 
 
