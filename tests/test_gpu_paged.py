@@ -210,6 +210,31 @@ def test_verify_varlen(preset, paged, case):
 
 
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_verify_max_rows(preset):
+    """The largest step the library takes: 128 queries x 64 query heads per
+    KV head = 8192 rows (the row -> (query, head) split at its limit),
+    causal, against the oracle; one more query head is refused."""
+    rng = np.random.default_rng(62)
+    B, Hq, Hk, N, S = 1, 64, 1, 128, 150
+    K, V = _kv(rng, B, S, Hk)
+    Q = rng.standard_normal((N, B, Hq, 128)).astype(np.float16)
+    sl = np.array([S], np.int32)
+    si, po = synth.token_lists(B, S)
+    print("max rows", PNAME[preset], flush=True)
+    contig = np.zeros(oracle.cache_bytes(preset, B, Hk, S), np.uint8)
+    oracle.store(preset, contig, B, Hk, S, K[si, po], V[si, po], si, po)
+    ref = oracle.verify(preset, contig, B, Hk, S, Q, sl, Hq, True)
+    cache = tq.Cache(preset, B, Hk, S)
+    tq.tqkv_store(cache, to_dev(np.ascontiguousarray(K[si, po])), to_dev(np.ascontiguousarray(V[si, po])),
+                  to_dev(si), to_dev(po))
+    out = tq.tqkv_verify(cache, to_dev(Q), to_dev(sl), N, Hq, True)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, what="8192 rows")
+    with pytest.raises(tq.TqkvError):
+        tq.tqkv_verify(cache, to_dev(np.zeros((N, B, 72, 128), np.float16)), to_dev(sl), N, 72, True)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
 @pytest.mark.parametrize("N", [16, 40, 128])
 def test_verify_many_queries(preset, N):
     """Dense steps beyond 8 queries (continuation chunks): up to 1024 rows
