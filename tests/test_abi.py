@@ -31,6 +31,20 @@ def test_binding_names_match_header():
         assert hasattr(tq, n), n
 
 
+def test_enum_values_match_header():
+    """The binding's preset, query-type and status constants are the values
+    include/tqkv.h gives them."""
+    src = open(os.path.join(ROOT, "include", "tqkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    vals = {k: int(v) for k, v in re.findall(r"\b(TQKV_[A-Z0-9_]+)\s*=\s*(-?\d+)", src)}
+    assert vals["TQKV_K8V4"] == tq.K8V4 and vals["TQKV_K3V4_NC"] == tq.K3V4_NC and vals["TQKV_K4V4_NC"] == tq.K4V4_NC
+    assert vals["TQKV_Q_F32"] == tq.Q_F32 and vals["TQKV_Q_F16"] == tq.Q_F16
+    assert vals["TQKV_OK"] == 0 and all(v < 0 for k, v in vals.items() if k.startswith("TQKV_ERR_"))
+    defines = dict(re.findall(r"#define\s+(TQKV_\w+)\s+(\d+)", src))
+    assert int(defines["TQKV_HEAD_DIM"]) == tq.HEAD_DIM and int(defines["TQKV_BLOCK_TOKENS"]) == tq.BLOCK_TOKENS
+    assert int(defines["TQKV_MAX_QLEN"]) == tq.MAX_QLEN
+
+
 def test_sizes():
     assert tq.tqkv_slot_bytes(tq.K3V4_NC) == 120
     assert tq.tqkv_slot_bytes(tq.K4V4_NC) == 136
