@@ -40,11 +40,15 @@ PINS = {
     "wht128": "closed form H_ij=(-1)^popcount(i&j); orthogonality; self-inverse",
     "tree_sumsq": "binary64 sum of squares within the binary32 error bound",
     "quant_key_k3 / quant_key_k4": "norm correction |khat| = n; distortion vs Gaussian-model MSE; nearest "
-                                   "level; zero vector",
+                                   "level; n_h = binary16 of the float64 norm; zero vector",
+    "lloyd_code": "ties on a threshold go to the upper cell, one ulp below to the lower; NaN -> 0",
+    "dequant": "Lloyd-Max keys: norm n and cosine to H k from the distortion model; FP8 keys within "
+               "2^-4; values within half a step",
     "quant_key_k8": "e4m3 relative error bound 2^-4; saturation never triggered",
     "quant_val": "|v - vhat| <= scale/2; endpoints hit codes 0 and 15; constant vector exact",
     "record layout": "parity unpinned (a layout choice): round trip pack/unpack and worked bytes only",
-    "verify": "torch SDPA in float64 on materialised K/V; brute-force special cases; causality",
+    "verify": "torch SDPA in float64 on materialised K/V; brute-force special cases; causality; rows "
+              "that see no token are NaN",
     "store_paged / gather_pages": "a paged store gathered through its block table equals the contiguous "
                                   "store byte for byte (layout: parity unpinned, as above)",
     "verify_varlen": "equal query counts reduce to verify; each sequence equals a one-sequence verify "
@@ -92,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.tqo_tree_sumsq_f32.restype = ctypes.c_float
         L.tqo_quant_key_k3.argtypes = [P, P, P, P, P, P]
         L.tqo_quant_key_lm.argtypes = [i32, P, P, P, P, P, P]
+        L.tqo_lloyd_code.argtypes = [i32, P, ctypes.c_float]
+        L.tqo_lloyd_code.restype = i32
         L.tqo_quant_key_k8.argtypes = [P, P, P]
         L.tqo_quant_val.argtypes = [P, P, P, P]
         L.tqo_block_bytes.argtypes = [i32]
@@ -158,6 +164,12 @@ def codebook(levels: int = 8):
     t = np.zeros(levels - 1, np.float32)
     lib().tqo_codebook_n(levels, _p(c), _p(t))
     return c, t
+
+
+def lloyd_code(levels: int, y: float) -> int:
+    """The cell of a rotated coordinate y against the levels-level thresholds."""
+    _, t = codebook(levels)
+    return int(lib().tqo_lloyd_code(levels, _p(t), float(y)))
 
 
 def key_levels(preset: int) -> int:

@@ -253,6 +253,17 @@ float tqo_tree_sumsq_f32(const float *x)
 /* Quantisers (one token-head vector of D = 128 binary16 values).            */
 /* ------------------------------------------------------------------------ */
 
+/* The Lloyd-Max cell of y: #{ j : y >= tau_j } over the nl - 1 thresholds,
+ * so a value on a threshold goes to the upper cell and NaN to cell 0 [R5]. */
+int tqo_lloyd_code(int nl, const float *th, float y)
+{
+    int c = 0;
+    for (int j = 0; j < nl - 1; ++j)
+        if (y >= th[j])
+            c++;
+    return c;
+}
+
 /* Lloyd-Max keys (k3v4_nc: nl = 8, k4v4_nc: nl = 16): norm, rotation,
  * codes against the nl-level codebook, norm correction.
  *   n     = sqrtf(tree sum of x^2)
@@ -272,11 +283,7 @@ void tqo_quant_key_lm(int nl, const uint16_t *kh, const float *cb, const float *
     tqo_wht128_f32(z);
     float r = 1.0f / (sqrtf(128.0f) * n);
     for (int i = 0; i < TQO_D; ++i) {
-        float y = z[i] * r;
-        int c = 0;
-        for (int j = 0; j < nl - 1; ++j)
-            if (y >= th[j])
-                c++;
+        int c = tqo_lloyd_code(nl, th, z[i] * r);
         codes[i] = (uint8_t)c;
         chat[i] = cb[c];
     }

@@ -77,7 +77,7 @@ def test_store_edge_vectors(preset):
         np.zeros(128), np.full(128, 1.5), np.full(128, -3.0), rng.standard_normal(128) * 1e-4,
         rng.standard_normal(128) * 3e4, np.where(rng.random(128) < 0.5, 0.0, -0.0),
         np.round(rng.standard_normal(128) * 4) / 4, np.arange(128) - 64.0, (np.arange(128) % 16) * 0.5,
-        rng.standard_normal(128) * 1e-6,
+        rng.standard_normal(128) * 1e-6, np.concatenate([[-0.0], np.linspace(0.1, 3.0, 127)]),
     ]
     T = len(vecs)
     K = np.stack(vecs).astype(np.float16)[:, None, :]

@@ -151,6 +151,43 @@ def test_values_error_bound_and_endpoints():
         assert codes.max() <= 15
 
 
+@pytest.mark.parametrize("levels", [8, 16])
+def test_lloyd_code_ties_go_up(levels):
+    """[R5]: a coordinate exactly on a threshold is coded into the upper cell,
+    one ulp below it into the lower one; NaN gives cell 0; the cells of the
+    levels themselves are their own indices."""
+    c, t = oracle.codebook(levels)
+    for j, tj in enumerate(t):
+        assert oracle.lloyd_code(levels, tj) == j + 1
+        assert oracle.lloyd_code(levels, np.nextafter(tj, np.float32(-np.inf))) == j
+    assert oracle.lloyd_code(levels, float("nan")) == 0
+    assert [oracle.lloyd_code(levels, x) for x in c] == list(range(levels))
+
+
+@pytest.mark.parametrize("preset", list(LM_KEYS))
+def test_lm_norm_is_the_rounded_norm(preset):
+    """n_h is the binary16 rounding of the key's norm: the binary32 tree sum
+    only moves it across a rounding boundary when the norm lies within about
+    2^-23 (relative) of one, so (almost) every key matches the float64 norm
+    rounded to binary16."""
+    quant, _, _ = LM_KEYS[preset]
+    rng = np.random.default_rng(25)
+    same = 0
+    for _ in range(400):
+        k = (rng.standard_normal(128) * rng.uniform(0.1, 10)).astype(np.float16)
+        _, nh, _ = quant(k)
+        same += nh == int(np.float16(np.linalg.norm(k.astype(np.float64))).view(np.uint16))
+    assert same >= 398
+
+
+def test_values_zero_point_is_positive_zero():
+    """[R9]: a minimum of -0 is stored as the zero point +0."""
+    v = np.linspace(0, 3, 128).astype(np.float16)
+    v[0] = np.float16(-0.0)  # the first (and only) minimum
+    _, _, zh = oracle.quant_val(v)
+    assert zh == 0x0000
+
+
 def test_values_constant_vector_exact():
     v = np.full(128, 1.5, np.float16)
     codes, sh, zh = oracle.quant_val(v)
@@ -278,6 +315,39 @@ def test_record_round_trip_and_slot_size(preset):
                             0xFFFF, 0xFFFF)
         seen += (b2 != 0)
     assert np.all(seen == 1)
+
+
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
+def test_dequant_reconstructs_the_token(preset):
+    """What the oracle's verify attends to, read back from a stored cache:
+    Lloyd-Max keys come back in the rotated space with the key's norm (the
+    norm correction) and close to H k; FP8 keys within the E4M3 relative
+    error; values within half a quantisation step."""
+    from tests import synth
+    rng = np.random.default_rng(28)
+    B, Hk, S = 1, 2, 24
+    K = (rng.standard_normal((B, S, Hk, 128)) * rng.uniform(0.2, 5, (B, S, Hk, 1))).astype(np.float16)
+    V = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+    cache = np.zeros(oracle.cache_bytes(preset, B, Hk, S), np.uint8)
+    si, po = synth.token_lists(B, S)
+    oracle.store(preset, cache, B, Hk, S, synth.rows(K), synth.rows(V), si, po)
+    H = _hadamard()
+    for t in range(S):
+        for hk in range(Hk):
+            k = K[0, t, hk].astype(np.float64)
+            v = V[0, t, hk].astype(np.float64)
+            khat, vhat = oracle.dequant(preset, cache, Hk, S, 0, hk, t)
+            if preset == oracle.K8V4:
+                assert np.all(np.abs(khat - k) <= 2.0 ** -4 * np.abs(k) + 2.0 ** -9 * np.abs(k).max() / 448)
+            else:
+                n = np.linalg.norm(k)
+                assert abs(np.linalg.norm(khat) - n) <= 3 * 2.0 ** -11 * n
+                cos = khat @ (H @ k) / (np.linalg.norm(khat) * n)
+                # the Gaussian-model distortion (0.0345 / 0.0095) puts the mean
+                # cosine near 0.983 / 0.995; a wrong or missing rotation gives ~0
+                assert cos > (0.95 if preset == oracle.K3V4_NC else 0.98), cos
+            _, vs, vz = oracle.quant_val(V[0, t, hk])
+            assert np.all(np.abs(vhat - v) <= h2f(vs) / 2 + 2.0 ** -10 * np.abs(v).max())
 
 
 def test_store_writes_the_quantised_record():

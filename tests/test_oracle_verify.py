@@ -150,6 +150,24 @@ def test_causality_invariance(preset):
     assert not np.allclose(a[2:], b[2:])
 
 
+@pytest.mark.parametrize("preset", [oracle.K8V4, oracle.K3V4_NC, oracle.K4V4_NC])
+def test_rows_without_visible_tokens_are_nan(preset):
+    """[R17]: with fewer tokens than queries (seq_len 3, n_spec 8, causal),
+    query n sees cached + n + 1 = n - 4 tokens: rows 0..4 see none and are
+    NaN, rows 5..7 match float64 SDPA over the tokens they see."""
+    rng = np.random.default_rng(39)
+    N, B, Hq, Hk, S, L = 8, 1, 2, 1, 16, 3
+    K = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+    V = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+    Q = rng.standard_normal((N, B, Hq, 128)).astype(np.float32)
+    cache = _build(preset, B, Hk, S, K, V)
+    sl = np.array([L], np.int32)
+    got = oracle.verify(preset, cache, B, Hk, S, Q, sl, Hq, True)
+    assert np.all(np.isnan(got[:5])) and np.all(np.isfinite(got[5:]))
+    ref = _sdpa_reference(preset, cache, B, Hk, S, Q[5:], sl, Hq, True)
+    assert np.allclose(got[5:], ref, rtol=1e-12, atol=1e-12)
+
+
 def test_mha_case_hq_equals_hk():
     rng = np.random.default_rng(37)
     N, B, H, S = 2, 1, 3, 18
