@@ -113,6 +113,10 @@ struct VerifyArgs {
     uint8_t *wbase; // the cache, writable (== base)
 };
 
+// Output rows per block of the key-range merge (32 lanes per row); the
+// merge launches 32 / kCombineRows blocks per (unit, 32-row tile).
+constexpr int kCombineRows = 4;
+
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
 hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const VerifyArgs &a, hipStream_t s);
