@@ -62,13 +62,18 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_digest():
-    """sha256 over the sources the verify kernel is built from: counter
-    readings taken on another version of the kernel are not reported."""
+    """sha256 over the code (comments and blank space removed) of the sources
+    the verify kernel is built from: counter readings taken on another
+    version of the kernel are not reported, edits to comments keep them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in ("verify.hip", "quant.h", "common.h", "codebook.h", "api.hip"):
-        with open(os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "quantized_kv_attention_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)    # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                   # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 
@@ -85,7 +90,7 @@ def recorded_traffic(workload):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    if fields.get("kernel_code_sha256") != kernel_source_digest():
         return None
     try:
         return int(fields["hbm_bytes_per_verify_call"])

@@ -8,28 +8,34 @@
 // softmax states with a log-sum-exp reduction.
 //
 // MI355X design (not the pages' Triton/SYCL design):
-//  * One work-group = 4 wavefronts = one (b, hk) unit and one key range.  A
-//    wavefront owns ALL R = (Hq/Hk) * N_spec query rows of its KV head (up to
-//    64) and a contiguous run of 32-token tiles, so every key/value code is
-//    fetched from HBM and dequantised exactly once per launch.
+//  * One work-group = 4 wavefronts = one (b, hk) unit, one key range and one
+//    group of query rows: the R = (Hq/Hk) * N_spec rows of a KV head are cut
+//    into 32-row tiles (one MFMA operand height), and a work-group takes one
+//    tile (two work-groups per compute unit) or two (64 rows, one per
+//    compute unit, each key/value tile dequantised once for all 64 rows).
+//    Each wavefront streams a contiguous run of 32-token tiles through its
+//    own LDS ring (direct global->LDS loads).
 //  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_f16: keys /
-//    value codes are the A operand (M = tokens or d), the 64 query rows the B
+//    value codes are the A operand (M = tokens or d), the query rows the B
 //    operand (N).  The C layout then gives each lane one query row and 16
 //    tokens, so the softmax row max needs a single cross-half swap and the
 //    probabilities become the next B operand without any data movement.
+//    Units of at most 8 rows (plain decode) use the transposed product
+//    S = Q K^T instead: one token per lane, 4 exponentials per lane per tile.
 //  * The packed layout is chosen so that each lane loads its MFMA operand
-//    bytes directly: 24 B of 3-bit codes or 64 B of FP8 per token half, and
-//    one 16 B load of value nibbles per 16-token block (8-token runs at a
-//    fixed d).  3-bit codes become fp16 centroids with v_perm_b32 table
-//    lookups (no LDS); FP8 becomes fp16 with v_cvt_scalef32_pk_f16_fp8.
-//  * Per-token factors stay out of the contraction: the key scale multiplies
-//    the score column, the value scale multiplies P, the value zero enters
-//    through sum_t p_t * zero_t.  Value codes enter the MFMA as the binary16
-//    integers c (low nibble) and 16c (high nibble), built with one mask.
+//    bytes directly: 24 B of 3-bit codes, 32 B of 4-bit codes or 64 B of FP8
+//    per token half, and one 16 B load of value nibbles per 16-token block
+//    (8-token runs at a fixed d).  Lloyd-Max codes become fp16 levels with
+//    v_perm_b32 table lookups (no LDS); FP8 becomes fp16 with
+//    v_cvt_scalef32_pk_f16_fp8.
+//  * Per-token factors: the key factor (FP8 scale, or n * gamma) scales the
+//    key operand, the value scale multiplies P, the value zero enters through
+//    sum_t p_t * zero_t.  Value codes enter the MFMA as the binary16
+//    subnormals c and 16c (low / high nibble), built with one mask.
 //  * The query operands are prepared inside the kernel (scale, WHT rotation
-//    for k3v4_nc as one small MFMA product with a +-1 matrix, fp16) and held
-//    in registers for the whole key loop; the output accumulators live in
-//    AGPRs, which the MFMAs read and write directly.
+//    for the Lloyd-Max presets as one small MFMA product with a +-1 matrix,
+//    fp16) and held in AGPRs for the whole key loop; the accumulators stay
+//    in VGPRs, where the rare online-softmax rescale reaches them.
 //  * The four wavefronts merge their softmax states through LDS; with more
 //    than one key range per unit a second kernel merges the ranges.
 #include "codebook.h"
