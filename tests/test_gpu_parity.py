@@ -123,6 +123,24 @@ def test_verify_small(preset, causal, q_dtype):
 
 
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("scale", [0.02, 0.15])
+def test_verify_explicit_scale(preset, scale):
+    """A caller's softmax scale (instead of 1/sqrt(D) = 0.088), in both the
+    64-row and the transposed few-row paths.  (The binary16 operands' score
+    error grows with the scale: at 0.3 one output in 32768 of this case sat
+    at the atol 5e-3 / rtol 1e-2 bound.)"""
+    for shape in (dict(N=8, Hq=16, Hk=2), dict(N=2, Hq=4, Hk=1)):
+        cfg = _small(preset, **shape)
+        inp = synth.make_inputs(cfg)
+        print("verify scale", PNAME[preset], scale, shape, flush=True)
+        ocache = _oracle_cache(cfg, inp)
+        ref = oracle.verify(preset, ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"], inp["seq_lens"],
+                            cfg["Hq"], cfg["causal"], sm_scale=scale)
+        cache = gpu_store_all(cfg, inp)
+        assert_close(_gpu_verify(cache, cfg, inp, sm_scale=scale), ref, what="sm_scale=%g" % scale)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
 @pytest.mark.parametrize("shape", [
     dict(N=1, Hq=1, Hk=1, B=1, S=17),          # one row, partial block
     dict(N=1, Hq=32, Hk=8, B=3, S=100),        # plain decode, 4 rows per KV head

@@ -23,7 +23,7 @@ def _build(preset, B, Hk, S, K, V, max_seq=None):
     return cache
 
 
-def _sdpa_reference(preset, cache, B, Hk, max_seq, Q, seq_lens, Hq, causal):
+def _sdpa_reference(preset, cache, B, Hk, max_seq, Q, seq_lens, Hq, causal, scale=None):
     """Materialise khat/vhat with the oracle's dequant, then attend with
     torch.nn.functional.scaled_dot_product_attention in float64."""
     N = Q.shape[0]
@@ -47,7 +47,7 @@ def _sdpa_reference(preset, cache, B, Hk, max_seq, Q, seq_lens, Hq, causal):
                         mask[n, L - N + n + 1:] = False
                 o = torch.nn.functional.scaled_dot_product_attention(
                     torch.tensor(q)[None, None], Kh[None, None], Vh[None, None],
-                    attn_mask=mask[None, None], scale=1 / np.sqrt(128.0))
+                    attn_mask=mask[None, None], scale=scale or 1 / np.sqrt(128.0))
                 out[:, b, hq] = o[0, 0].numpy()
     return out
 
@@ -166,6 +166,23 @@ def test_rows_without_visible_tokens_are_nan(preset):
     assert np.all(np.isnan(got[:5])) and np.all(np.isfinite(got[5:]))
     ref = _sdpa_reference(preset, cache, B, Hk, S, Q[5:], sl, Hq, True)
     assert np.allclose(got[5:], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+def test_explicit_softmax_scale(scale):
+    """A caller's softmax scale replaces 1/sqrt(D) exactly as SDPA's scale does."""
+    rng = np.random.default_rng(40)
+    N, B, Hq, Hk, S = 4, 1, 4, 2, 40
+    K = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+    V = rng.standard_normal((B, S, Hk, 128)).astype(np.float16)
+    Q = rng.standard_normal((N, B, Hq, 128)).astype(np.float32)
+    sl = np.array([S], np.int32)
+    for preset in (oracle.K8V4, oracle.K4V4_NC):
+        cache = _build(preset, B, Hk, S, K, V)
+        got = oracle.verify(preset, cache, B, Hk, S, Q, sl, Hq, True, sm_scale=scale)
+        ref = _sdpa_reference(preset, cache, B, Hk, S, Q, sl, Hq, True, scale=scale)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+        assert not np.allclose(got, oracle.verify(preset, cache, B, Hk, S, Q, sl, Hq, True), atol=1e-3)
 
 
 def test_mha_case_hq_equals_hk():
