@@ -267,13 +267,37 @@ __device__ inline uint32_t hmul2(uint32_t a, uint32_t b)
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
 }
 
+// n * gamma of token tok of a Lloyd-Max block, in binary32 (the product of
+// two binary16 values is exact there)
+template <typename L> __device__ inline float key_factor(const uint8_t *blk, int tok)
+{
+    const uint16_t n = *reinterpret_cast<const uint16_t *>(blk + L::kMeta0 + 2 * (tok & 15));
+    const uint16_t g = *reinterpret_cast<const uint16_t *>(blk + L::kMeta1 + 2 * (tok & 15));
+    return h2f(n) * h2f(g);
+}
+
+// Byte tables (lo 0-3, lo 4-7, hi 0-3, hi 4-7) of the 8 binary16 values
+// lv[j] * f, each rounded once from binary32, for v_perm_b32 lookups.
+__device__ inline void level_table(uint32_t (&tab)[4], const float *lv, float f)
+{
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        c[j] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(lv[2 * j] * f), (_Float16)(lv[2 * j + 1] * f)});
+    tab[0] = perm(c[1], c[0], 0x06040200u);
+    tab[1] = perm(c[3], c[2], 0x06040200u);
+    tab[2] = perm(c[1], c[0], 0x07050301u);
+    tab[3] = perm(c[3], c[2], 0x07050301u);
+}
+
 // The lane's key codes and key factor.  The factor (the per-token key scale,
 // or n * gamma) multiplies the key operand instead of the score column: for
 // FP8 with one packed fp16 multiply per code pair (the scale operand of
 // v_cvt_scalef32_pk_f16_fp8 only applies a power of two), for the 3- and
-// 4-bit codes through a per-lane table of 8 scaled levels (4 multiplies + 4
-// byte permutes per tile; the 16-level codebook is symmetric, so its table
-// holds the magnitudes and the code's sign bit becomes the fp16 sign).
+// 4-bit codes through a per-lane table of 8 scaled levels (binary32 products
+// rounded once to binary16, then 4 byte permutes per tile; the 16-level
+// codebook is symmetric, so its table holds the magnitudes and the code's
+// sign bit becomes the fp16 sign).
 template <int PRESET>
 __device__ inline void read_keys(KeyRegs<PRESET> &t, const uint8_t *slot, int lane)
 {
@@ -286,35 +310,13 @@ __device__ inline void read_keys(KeyRegs<PRESET> &t, const uint8_t *slot, int la
 #pragma unroll
         for (int j = 0; j < 3; ++j)
             t.k[j] = *reinterpret_cast<const uint2 *>(kb + 24 * h + 8 * j);
-        const uint32_t n = *reinterpret_cast<const uint16_t *>(blk + L::kMeta0 + 2 * (tok & 15));
-        const uint32_t g = *reinterpret_cast<const uint16_t *>(blk + L::kMeta1 + 2 * (tok & 15));
-        const uint32_t f = hmul2(n, g);          // n * gamma in the low half
-        const uint32_t ff = f | (f << 16);       // ... in both halves
-        const uint32_t c01 = hmul2(kCentroidHalf[0] | ((uint32_t)kCentroidHalf[1] << 16), ff);
-        const uint32_t c23 = hmul2(kCentroidHalf[2] | ((uint32_t)kCentroidHalf[3] << 16), ff);
-        const uint32_t c45 = hmul2(kCentroidHalf[4] | ((uint32_t)kCentroidHalf[5] << 16), ff);
-        const uint32_t c67 = hmul2(kCentroidHalf[6] | ((uint32_t)kCentroidHalf[7] << 16), ff);
-        t.tab[0] = perm(c23, c01, 0x06040200u);
-        t.tab[1] = perm(c67, c45, 0x06040200u);
-        t.tab[2] = perm(c23, c01, 0x07050301u);
-        t.tab[3] = perm(c67, c45, 0x07050301u);
+        level_table(t.tab, kCentroid, key_factor<L>(blk, tok));
     } else if constexpr (PRESET == kPresetK4V4) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             t.k[j] = *reinterpret_cast<const u32x4 *>(kb + 32 * h + 16 * j);
-        const uint32_t n = *reinterpret_cast<const uint16_t *>(blk + L::kMeta0 + 2 * (tok & 15));
-        const uint32_t g = *reinterpret_cast<const uint16_t *>(blk + L::kMeta1 + 2 * (tok & 15));
-        const uint32_t f = hmul2(n, g);
-        const uint32_t ff = f | (f << 16);
         // magnitudes: levels 8..15 of the ascending codebook
-        const uint32_t c01 = hmul2(kCentroidHalf16[8] | ((uint32_t)kCentroidHalf16[9] << 16), ff);
-        const uint32_t c23 = hmul2(kCentroidHalf16[10] | ((uint32_t)kCentroidHalf16[11] << 16), ff);
-        const uint32_t c45 = hmul2(kCentroidHalf16[12] | ((uint32_t)kCentroidHalf16[13] << 16), ff);
-        const uint32_t c67 = hmul2(kCentroidHalf16[14] | ((uint32_t)kCentroidHalf16[15] << 16), ff);
-        t.tab[0] = perm(c23, c01, 0x06040200u);
-        t.tab[1] = perm(c67, c45, 0x06040200u);
-        t.tab[2] = perm(c23, c01, 0x07050301u);
-        t.tab[3] = perm(c67, c45, 0x07050301u);
+        level_table(t.tab, kCentroid16 + 8, key_factor<L>(blk, tok));
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
