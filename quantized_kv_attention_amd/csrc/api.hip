@@ -145,7 +145,7 @@ bool grid_fits(const View &c, int rows, int splits)
 {
     const long rt = row_tiles(rows), nqt = rows_per_group(rows);
     const long verify_groups = (long)c.B * c.Hk * splits * ((rt + nqt - 1) / nqt);
-    const long combine_groups = splits > 1 ? (long)c.B * c.Hk * rt * (32 / kCombineRows) : 0;
+    const long combine_groups = splits > 1 ? (long)c.B * c.Hk * rt * 4 * combine_groups_per_row(splits) : 0;
     return verify_groups <= INT32_MAX && combine_groups <= INT32_MAX;
 }
 

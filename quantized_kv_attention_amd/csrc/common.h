@@ -113,9 +113,13 @@ struct VerifyArgs {
     uint8_t *wbase; // the cache, writable (== base)
 };
 
-// Output rows per block of the key-range merge (32 lanes per row); the
-// merge launches 32 / kCombineRows blocks per (unit, 32-row tile).
-constexpr int kCombineRows = 4;
+// Lane groups of 32 that merge one output row of the key-range merge (at
+// most 8 ranges per group up to 64 ranges); the merge launches 4 * that
+// many blocks of 256 threads per (unit, 32-row tile).
+inline int combine_groups_per_row(int nsplit)
+{
+    return nsplit <= 8 ? 1 : nsplit <= 16 ? 2 : nsplit <= 32 ? 4 : 8;
+}
 
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);

@@ -152,6 +152,41 @@ __device__ inline void dma16_s(const void *base, uint32_t off, uint32_t lds_base
 }
 #pragma clang diagnostic pop
 
+// Loads 4g .. 4g + n - 1 of a tile: one M0 write, then immediate offsets
+// (global_load_lds adds the instruction offset to the global address and to
+// the LDS destination alike); the tile's last load takes voff_last.
+template <int N, bool LAST>
+__device__ inline void dma_group(const void *base, uint32_t voff, uint32_t voff_last, uint32_t lds_base)
+{
+    static_assert(N >= 1 && N <= 4, "group size");
+    const uint32_t vl = LAST ? voff_last : voff;
+    if constexpr (N == 1) {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %1"
+                     :
+                     : "v"(voff), "s"(base), "s"(lds_base), "v"(vl)
+                     : "memory", "m0");
+    } else if constexpr (N == 2) {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %3, %1 offset:1024"
+                     :
+                     : "v"(voff), "s"(base), "s"(lds_base), "v"(vl)
+                     : "memory", "m0");
+    } else if constexpr (N == 3) {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024\n\tglobal_load_lds_dwordx4 %3, %1 offset:2048"
+                     :
+                     : "v"(voff), "s"(base), "s"(lds_base), "v"(vl)
+                     : "memory", "m0");
+    } else {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024\n\tglobal_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                     "global_load_lds_dwordx4 %3, %1 offset:3072"
+                     :
+                     : "v"(voff), "s"(base), "s"(lds_base), "v"(vl)
+                     : "memory", "m0");
+    }
+}
+
 // Issue the loads of tile kt (blocks 2kt, 2kt+1 of this unit) into the
 // ring slot at LDS address slot_lds.  Load j covers tile bytes
 // [1024 j, 1024 j + 1024); the last load's lanes past the tile end re-read
@@ -167,10 +202,13 @@ __device__ inline void issue_tile(const uint8_t *ubase, int kt, int nblk, uint32
     constexpr int LPT = Ring<PRESET, 1>::kLoads;
     const uint8_t *src = ubase + (size_t)(2 * kt) * L::kBlockBytes;
     if (__builtin_expect(2 * kt + 1 < nblk, 1)) {
-#pragma unroll
-        for (int j = 0; j < LPT - 1; ++j)
-            dma16_s(src + 1024 * j, voff, slot_lds + 1024 * j);
-        dma16_s(src + 1024 * (LPT - 1), voff_last, slot_lds + 1024 * (LPT - 1));
+        if constexpr (LPT <= 4) {
+            dma_group<LPT, true>(src, voff, voff_last, slot_lds);
+        } else {
+            static_assert(LPT <= 8, "loads per tile");
+            dma_group<4, false>(src, voff, voff_last, slot_lds);
+            dma_group<LPT - 4, true>(src + 4096, voff, voff_last, slot_lds + 4096);
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < LPT; ++j)
@@ -446,9 +484,10 @@ __device__ inline half8_t value_operand(const u32x4 (&v)[2], int dt, int s)
 
 // Lazy rescaling: the running row maximum m only moves when a tile's maximum
 // exceeds it by more than kRescaleSlack (log2 units), so probabilities are
-// at most 2^kRescaleSlack = 4.  With value scales below 2^14 (every binary16
-// min-max scale is), P * vscale <= 4 * 8736 stays inside binary16 range.
-constexpr float kRescaleSlack = 2.0f;
+// below 2^2.9 < 7.47.  The largest binary16 min-max value scale is
+// f16((65504 + 65504) / 15) = 8736, and 7.47 * 8736 < 65504: P * vscale
+// stays inside binary16 range.
+constexpr float kRescaleSlack = 2.9f;
 
 // Online-softmax state of the lane's query rows (one per 32-row tile).
 template <int NQT> struct SoftState {
@@ -1355,31 +1394,651 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     }
 }
 
-// Merge of the key ranges of each (b, hk, row tile): out = sum_s w_s O_s /
-// sum_s w_s with w_s = exp2(m_s - max_s m_s) * l_s, in a fixed order.  One
-// 32-lane group per row, one float4 of the row per lane; every lane loads
-// the row's (m, l) pairs and its own partial float4s in one batch, so the
-// kernel costs a single round trip to memory.  Ranges whose softmax sum is
-// exactly 0 saw no token and get weight 0; a NaN sum reaches the output.
-// Blocks are dealt to the XCDs like the verify work-groups of the same
-// rows, so the partial states are read where they were written.  Blocks of
-// kCombineRows rows (4: 128 threads) spread the merge over every compute
-// unit (PoC: 256 blocks; blocks of 8 rows left half of them idle and took
-// 0.4-0.7 us more per PoC call, 2 us more at long context).
-constexpr int kCombineChunk = 16;
-
-__global__ __launch_bounds__(32 * kCombineRows) void combine_kernel(VerifyArgs a)
+// A operand of k-step ks of S^T = K Q^T from FP8 codes, without the key
+// scale (it multiplies the score column instead).
+__device__ inline half8_t key_operand_fp8(const KeyRegs<kPresetK8V4> &t, int ks)
 {
-    constexpr int kBlocksPerTile = 32 / kCombineRows;
+    const uint32_t a = t.k[ks >> 1][2 * (ks & 1)], b = t.k[ks >> 1][2 * (ks & 1) + 1];
+    H8 o;
+    o.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false));
+    o.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true));
+    o.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
+    o.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true));
+    return o.h;
+}
+
+__device__ inline float max16(const floatx16 &x)
+{
+    float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+    for (int v = 3; v < 15; v += 2)
+        m = fmaxf(fmaxf(m, x[v]), x[v + 1]);
+    return fmaxf(m, x[15]);
+}
+
+// ---------------------------------------------------------------------------
+// Work-groups of 64 query rows: eight independent wavefronts.
+//
+// A wavefront on gfx950 issues one VALU instruction at most about every 8
+// cycles, while a SIMD accepts one about every 4 to 5 when two wavefronts
+// feed it, and the matrix core working for one wavefront overlaps the VALU
+// work of the other (measured with probe kernels).  The 64-row work-group
+// therefore runs two wavefronts per SIMD, each streaming its own run of
+// 32-token tiles through its own LDS ring and computing everything for all
+// 64 rows (each key and value tile is dequantised once): S = K Q^T, the
+// online softmax, O += P V and the row sums.  The two wavefronts of a SIMD
+// never wait for each other, so the stalls of one (LDS latency, matrix-core
+// results) are filled by the other's instructions.  To fit two wavefronts'
+// registers (256 each) the fp16 query operands stay in LDS and are read per
+// k-step; the accumulators (128 registers) stay in registers.
+// ---------------------------------------------------------------------------
+template <int PRESET> struct WideRing;
+template <> struct WideRing<kPresetK3V4> { static constexpr int kDepth = 4; };
+template <> struct WideRing<kPresetK4V4> { static constexpr int kDepth = 3; };
+template <> struct WideRing<kPresetK8V4> { static constexpr int kDepth = 2; };
+
+template <int PRESET, bool PAGED>
+__global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
+{
+    constexpr int NQT = 2, RP = 64, kW = 8;
+    constexpr int LPT = Ring<PRESET, 1>::kLoads, DEPTH = WideRing<PRESET>::kDepth;
+    constexpr int kSlotBytes = LPT * 1024;
+    // query rows: raw, then the fp16 operand rows in place (resident)
+    constexpr int kQRegion = RP * kD * 4;
+    static_assert(RP * kQStride * 2 <= kQRegion, "query region");
+    constexpr int kRingBytes = kW * DEPTH * kSlotBytes;
+    // merge: four wavefronts' accumulators at a time (register layout) and
+    // the (m, l, z) states of all eight
+    constexpr int kXBytes = 4 * NQT * 4 * 4 * 64 * 16;
+    constexpr int kMergeBytes = kXBytes + kW * RP * 16;
+    constexpr int kLdsBytes = (kQRegion + kRingBytes) > kMergeBytes ? (kQRegion + kRingBytes) : kMergeBytes;
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(DEPTH * LPT <= 63 && DEPTH <= 8, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    int item = blockIdx.x;
+    if ((gridDim.x & 7) == 0)
+        item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int nwt = (a.nrt + NQT - 1) / NQT;
+    const int rt = item % nwt, us = item / nwt;
+    const int unit = us / a.nsplit, split = us % a.nsplit;
+    const int row0 = RP * rt;
+    const int tile0 = NQT * rt;
+    const int b = unit / a.Hk, hk = unit % a.Hk;
+    const int Lr = a.seq_lens[b];
+    const int L = Lr < 0 ? 0 : (Lr > a.max_seq ? a.max_seq : Lr);
+    int nq = a.N, qt0 = b, qts = a.B;
+    if (a.cu_q) {
+        qt0 = a.cu_q[b];
+        nq = min(max(a.cu_q[b + 1] - qt0, 0), a.N);
+        qts = 1;
+    }
+    const int Rb = a.G * nq;
+    if (row0 >= Rb)
+        return;
+    const float rcpG = __builtin_amdgcn_rcpf((float)a.G);
+    auto row_token = [&](int r) { return (int)(((float)r + 0.5f) * rcpG); };
+
+    // the work-group's tiles [wt0, wt1).  The two wavefronts of a SIMD do
+    // not advance at the same rate (the older one is issued first), so the
+    // tiles are handed out on demand: wavefront w starts with tiles
+    // wt0 + w + kW j (j < DEPTH) and then claims one tile per step from a
+    // work-group counter, always in increasing order
+    const int tiles = (L + kTile - 1) / kTile;
+    const int tpw = (tiles + a.nsplit - 1) / a.nsplit;
+    const int wt0 = min(split * tpw, tiles), wt1 = min(wt0 + tpw, tiles);
+
+    using L_ = Layout<PRESET>;
+    const uint8_t *ubase = a.base + (size_t)unit * a.nblk * L_::kBlockBytes;
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_void_t *)lds;
+    const uint32_t ring_lds = lds0 + kQRegion + wave * DEPTH * kSlotBytes;
+    const uint8_t *ring = lds + kQRegion + wave * DEPTH * kSlotBytes;
+    _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
+
+    // ------------------------------------------------------------ prologue
+    // 1. raw query rows -> LDS, queued before any ring load
+    {
+        const int esz = a.q_f16 ? 2 : 4;
+        const int rshift = a.q_f16 ? 4 : 5;
+        const int rpi = 64 >> rshift;
+        const int rsub = lane >> rshift, cb = 16 * (lane & ((1 << rshift) - 1));
+        for (int J = wave; J < RP / rpi; J += kW) {
+            const int r = row0 + J * rpi + rsub;
+            const int rs = r < Rb ? r : 0;
+            const int n = row_token(rs), g = rs - n * a.G;
+            const uint8_t *src = static_cast<const uint8_t *>(a.Q) +
+                                 ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD * esz + cb;
+            dma16(src, lds0 + 1024 * J);
+        }
+    }
+    const int nbl = (L + kBlockTokens - 1) / kBlockTokens;
+    const int32_t *brow = PAGED ? a.btab + (size_t)b * a.bstride : nullptr;
+    __builtin_amdgcn_s_barrier();
+
+    // 2. the first ring tiles
+    const uint32_t voff = 16 * lane;
+    const uint32_t voff_last = (uint32_t)min(16 * lane, 2 * L_::kBlockBytes - 16 - 1024 * (LPT - 1));
+    int issued = 0; // tiles this wavefront has put in flight
+    // tile t (absolute index) into the ring slot at LDS address slot
+    auto issue = [&](int t, uint32_t slot) {
+        if constexpr (!PAGED) {
+            issue_tile<PRESET>(ubase, t, a.nblk, slot, voff, voff_last, lane);
+        } else {
+            // the page ids of the tile's two blocks (uniform loads; ids out
+            // of range read page 0, whose tokens the mask never admits)
+            const int j = 2 * t;
+            const bool two = j + 1 < nbl;
+            int p0 = brow[j], p1 = two ? brow[j + 1] : 0;
+            p0 = (p0 >= 0 && p0 < a.npages) ? p0 : 0;
+            p1 = (p1 >= 0 && p1 < a.npages) ? p1 : 0;
+            const uint8_t *src0 = a.base + ((size_t)p0 * a.Hk + hk) * L_::kBlockBytes;
+            const uint8_t *src1 = a.base + ((size_t)p1 * a.Hk + hk) * L_::kBlockBytes;
+            issue_tile_paged<PRESET>(src0, src1, two, slot, voff, voff_last, lane);
+        }
+    };
+    // the slot window: tq[j] is the tile in the j-th oldest slot in flight
+    // (wt1 or more: none)
+    int tq[DEPTH];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+        tq[j] = min(wt0 + wave + kW * j, wt1);
+    auto store_block = [&](int t) -> uint8_t * {
+        if constexpr (!PAGED) {
+            return a.wbase + ((size_t)unit * a.nblk + (t >> 4)) * L_::kBlockBytes;
+        } else {
+            const int p = brow[t >> 4];
+            return (p >= 0 && p < a.npages) ? a.wbase + ((size_t)p * a.Hk + hk) * L_::kBlockBytes : nullptr;
+        }
+    };
+    const int tn0 = (a.Knew != nullptr) ? L - nq : L;
+    const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile);
+    // tiles entirely before the new tokens go first
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+        if (issued == j && tq[j] < wt1 && (tq[j] + 1) * kTile <= tn0) {
+            issue(tq[j], ring_lds + j * kSlotBytes);
+            ++issued;
+        }
+
+    // 3. fused store of this work-group's share of the new tokens, spread
+    //    over the eight wavefronts; complete before any tile holding them is
+    //    loaded
+    if (wn0 < wn1) {
+        for (int t = wn0 + wave; t < wn1; t += 2 * kW) {
+            const int t2 = t + kW;
+            const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+            const size_t src2 = ((size_t)(qt0 + (min(t2, wn1 - 1) - tn0) * qts) * a.Hk + hk) * kD;
+            const quant::TokenHead x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+            const quant::TokenHead x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+            uint8_t *blk = store_block(t);
+            if (t2 < wn1) {
+                const quant::Record r1 = quant::quantize_record<PRESET>(x, lane);
+                const quant::Record r2 = quant::quantize_record<PRESET>(x2, lane);
+                uint8_t *blk2 = store_block(t2);
+                if (blk)
+                    quant::store_record<PRESET>(blk, t & 15, r1, lane);
+                if (blk2)
+                    quant::store_record<PRESET>(blk2, t2 & 15, r2, lane);
+            } else {
+                asm volatile("" ::"v"(x2.k0), "v"(x2.k1), "v"(x2.v0), "v"(x2.v1));
+                const quant::Record r1 = quant::quantize_record<PRESET>(x, lane);
+                if (blk)
+                    quant::store_record<PRESET>(blk, t & 15, r1, lane);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+        if (issued == j && tq[j] < wt1) {
+            issue(tq[j], ring_lds + j * kSlotBytes);
+            ++issued;
+        }
+
+    // 4. state
+    int erow[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const int rr = row0 + 32 * qt + col;
+        const int n = row_token(rr);
+        erow[qt] = (rr < Rb) ? (a.causal ? min(L - nq + n + 1, L) : L) : 0;
+    }
+    const int emin = a.causal ? (L - nq + 1) : L;
+    const int tmask = emin / kTile; // tiles from here on need the causal / length mask
+    // the claim counter lives past the binary16 query rows (written once the
+    // raw rows there have been read)
+    uint32_t *claim_ctr = reinterpret_cast<uint32_t *>(lds + kQRegion - 16);
+    static_assert(RP * kQStride * 2 <= kQRegion - 16, "claim counter");
+
+    wait_ring<LPT>(issued); // this wavefront's query loads have landed
+    lds_barrier();
+
+    // 5. scale and round to binary16 (thread t: 16 coordinates of row t / 8)
+    {
+        constexpr int CPT = 16, TPR = kD / CPT;
+        const int rr = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * CPT;
+        uint32_t qh[CPT / 2];
+        if (a.q_f16) {
+            const _Float16 *src = reinterpret_cast<const _Float16 *>(lds + rr * 256) + c0;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 8) {
+                const half8_t x = *reinterpret_cast<const half8_t *>(src + c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const half2_t p = half2_t{(_Float16)((float)x[2 * j] * a.qscale),
+                                              (_Float16)((float)x[2 * j + 1] * a.qscale)};
+                    qh[c / 2 + j] = __builtin_bit_cast(uint32_t, p);
+                }
+            }
+        } else {
+            const float *src = reinterpret_cast<const float *>(lds + rr * 512) + c0;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + c);
+                qh[c / 2] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale)});
+                qh[c / 2 + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale)});
+            }
+        }
+        if (row0 + rr >= Rb) {
+#pragma unroll
+            for (int j = 0; j < CPT / 2; ++j)
+                qh[j] = 0u;
+        }
+        lds_barrier();
+        uint32_t *dst = reinterpret_cast<uint32_t *>(qs + rr * kQStride + c0);
+#pragma unroll
+        for (int j = 0; j < CPT / 2; j += 4)
+            *reinterpret_cast<u32x4 *>(dst + j) = u32x4{qh[j], qh[j + 1], qh[j + 2], qh[j + 3]};
+        if (threadIdx.x == 0)
+            *claim_ctr = (uint32_t)(wt0 + kW * DEPTH);
+        lds_barrier();
+    }
+
+    // 6. Lloyd-Max keys: q' = H q / sqrt(128) as the MFMA product H Q^T;
+    //    wavefronts 0..3 compute output coordinates 32w..32w+31
+    if constexpr (kLloydMax<PRESET>) {
+        floatx16 C[NQT];
+        if (wave < 4) {
+            half8_t Bq[NQT][8];
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks)
+                    Bq[qt][ks] = *reinterpret_cast<const half8_t *>(qs + (32 * qt + col) * kQStride + 16 * ks + 8 * h);
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+                C[qt] = floatx16{0};
+            const int o = 32 * wave + col;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const half8_t A = hadamard_operand(o, ks, h);
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt)
+                    C[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bq[qt][ks], C[qt], 0, 0, 0);
+            }
+        }
+        lds_barrier();
+        if (wave < 4) {
+            constexpr float kInvSqrt128 = 0.08838834764831845f;
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const half2_t p0 = half2_t{(_Float16)(C[qt][4 * g] * kInvSqrt128), (_Float16)(C[qt][4 * g + 1] * kInvSqrt128)};
+                    const half2_t p1 = half2_t{(_Float16)(C[qt][4 * g + 2] * kInvSqrt128), (_Float16)(C[qt][4 * g + 3] * kInvSqrt128)};
+                    *reinterpret_cast<uint2 *>(qs + (32 * qt + col) * kQStride + 32 * wave + 8 * g + 4 * h) =
+                        make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+                }
+        }
+        lds_barrier();
+    }
+
+    // ------------------------------------------------------------ key loop
+    // the B operand of k-step ks of row tile qt: coordinates 64h + 8ks + 0..7
+    // of this lane's query row 32qt + col, read from LDS when needed
+    const _Float16 *qrow = qs + col * kQStride + 64 * h;
+    auto qop = [&](int qt, int ks) {
+        return *reinterpret_cast<const half8_t *>(qrow + 32 * qt * kQStride + 8 * ks);
+    };
+    floatx16 acc[4][NQT];
+    float m[NQT], msub[NQT], thr[NQT], ls[NQT], zs[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        m[qt] = -__builtin_inff();
+        msub[qt] = 0.0f;
+        thr[qt] = -__builtin_inff();
+        ls[qt] = 0.0f;
+        zs[qt] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            acc[dt][qt] = floatx16{0};
+    }
+    // tile i: S = K Q^T, the lazy online-softmax rescale (the running max
+    // moves only when a score exceeds it by more than kRescaleSlack; an
+    // unset max takes the tile's maximum), P = exp2(S - m) in binary16, the
+    // sums l, z, and O += V^T (P vscale)^T
+    auto step = [&](int i, int t, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int tok0 = t * kTile;
+        // tile i has landed (in the steady state DEPTH - 1 later tiles are
+        // in flight behind it)
+        if (issued - i == DEPTH)
+            wait_vm<(DEPTH - 1) * LPT>();
+        else
+            wait_ring<LPT>(issued - i - 1);
+        const uint8_t *slot = ring + (i % DEPTH) * kSlotBytes;
+        KeyRegs<PRESET> kr;
+        read_keys<PRESET>(kr, slot, lane);
+        H8 f[2];
+        if constexpr (!kLloydMax<PRESET>) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                f[s2].h = *reinterpret_cast<const half8_t *>(slot + s2 * L_::kBlockBytes + L_::kMeta0 + 16 * h);
+        }
+        floatx16 S[NQT];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            half8_t A;
+            if constexpr (kLloydMax<PRESET>)
+                A = key_operand<PRESET>(kr, ks);
+            else
+                A = key_operand_fp8(kr, ks);
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt)
+                S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qop(qt, ks), ks == 0 ? floatx16{0} : S[qt], 0, 0, 0);
+        }
+        // scores relative to the subtrahend (FP8: each column times its
+        // token's key scale); register v holds token tok0 + 8h + 16 (v / 8)
+        // + v % 8
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if constexpr (kLloydMax<PRESET>)
+                    S[qt][v] -= msub[qt];
+                else
+                    S[qt][v] = __builtin_fmaf(S[qt][v], (float)f[v >> 3].h[v & 7], -msub[qt]);
+            }
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int lim = erow[qt] - tok0 - 8 * h;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (16 * (v >> 3) + (v & 7) >= lim)
+                        S[qt][v] = -__builtin_inff();
+            }
+        }
+        float mx[NQT];
+        bool grow = false;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            mx[qt] = max16(S[qt]);
+            grow |= mx[qt] > thr[qt];
+        }
+        if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const float tmax = halves_max(mx[qt]) + msub[qt]; // the row's largest score of the tile
+                const float mnew = fmaxf(m[qt], tmax);
+                const float alpha = (m[qt] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m[qt] - mnew);
+                const float snew = (mnew == -__builtin_inff()) ? 0.0f : mnew;
+                const float d = snew - msub[qt];
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    S[qt][v] -= d;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    acc[dt][qt] *= alpha;
+                ls[qt] *= alpha;
+                zs[qt] *= alpha;
+                m[qt] = mnew;
+                msub[qt] = snew;
+                thr[qt] = (mnew == -__builtin_inff()) ? -__builtin_inff() : kRescaleSlack;
+            }
+        }
+        ValRegs vr;
+        read_values<PRESET>(vr, slot, lane);
+        if constexpr (MASKED) {
+            // fields of tokens past the sequence end never enter (they may hold anything)
+            const int lim = L - tok0 - 8 * h;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t keep = ((16 * s2 + 2 * j < lim) ? 0x0000FFFFu : 0u) |
+                                          ((16 * s2 + 2 * j + 1 < lim) ? 0xFFFF0000u : 0u);
+                    vr.vs[s2][j] &= keep;
+                    vr.vz[s2][j] &= keep;
+                }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                H8 Bp;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // (vector elements are copied to scalars first: a bit cast
+                    // of an ext_vector_type element reads element 0 in this
+                    // compiler)
+                    const uint32_t vsj = vr.vs[s2][j], vzj = vr.vz[s2][j];
+                    const float p0 = __builtin_amdgcn_exp2f(S[qt][8 * s2 + 2 * j]);
+                    const float p1 = __builtin_amdgcn_exp2f(S[qt][8 * s2 + 2 * j + 1]);
+                    const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
+                    ls[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls[qt], false);
+                    zs[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vzj), zs[qt], false);
+                    Bp.u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vsj));
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(vr.v, dt, s2), Bp.h, acc[dt][qt],
+                                                                         0, 0, 0);
+            }
+    };
+    // step i works on tile tq[0] in slot i % DEPTH; the tile claimed during
+    // the step refills that slot, and the window moves on
+    int i = 0;
+    bool more = true; // the counter may still hold tiles for this wavefront
+    auto claim = [&]() {
+        uint32_t c = 0u;
+        if (more && lane == 0)
+            c = __hip_atomic_fetch_add(claim_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return c;
+    };
+    auto advance = [&](uint32_t c) {
+        int nt = wt1;
+        if (more) {
+            nt = min((int)__builtin_amdgcn_readfirstlane(c), wt1);
+            more = nt < wt1;
+        }
+        if (nt < wt1) {
+            wait_lgkm0(); // the slot's LDS reads are complete
+            issue(nt, ring_lds + (i % DEPTH) * kSlotBytes);
+            ++issued;
+        }
+#pragma unroll
+        for (int j = 0; j + 1 < DEPTH; ++j)
+            tq[j] = tq[j + 1];
+        tq[DEPTH - 1] = nt;
+        ++i;
+    };
+    while (tq[0] < min(wt1, tmask)) {
+        const uint32_t c = claim();
+        step(i, tq[0], std::false_type{});
+        advance(c);
+    }
+    while (tq[0] < wt1) {
+        const uint32_t c = claim();
+        step(i, tq[0], std::true_type{});
+        advance(c);
+    }
+
+    // ---------------------------------------------------------------- merge
+    // Eight states per row (one per wavefront, over different tokens):
+    // first every (m, l, z), then the accumulators of wavefronts 4..7 and of
+    // 0..3 in two rounds through the same LDS area; wavefront w reduces
+    // C-register quad aa = w % 4 of row tile mq = w / 4.
+    float4 *xbuf = reinterpret_cast<float4 *>(lds); // [w % 4][qt][aa][dt][lane]
+    float4 *sbuf = reinterpret_cast<float4 *>(lds + kXBytes); // [w][row]: m, l, z
+    __syncthreads(); // every wavefront is done with the ring and the query rows
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        const float l2 = halves_sum(ls[qt]), z2 = halves_sum(zs[qt]);
+        if (h == 0)
+            sbuf[wave * RP + 32 * qt + col] = make_float4(m[qt], l2, z2, 0.0f);
+    }
+    const int mq = wave >> 2, aa = wave & 3, lrow = col;
+    auto put_acc = [&]() {
+        const int ww = wave & 3;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    xbuf[(((ww * NQT + qt) * 4 + a2) * 4 + dt) * 64 + lane] =
+                        make_float4(acc[dt][qt][4 * a2], acc[dt][qt][4 * a2 + 1], acc[dt][qt][4 * a2 + 2],
+                                    acc[dt][qt][4 * a2 + 3]);
+    };
+    if (wave >= 4)
+        put_acc();
+    __syncthreads();
+    float M = -__builtin_inff();
+    float4 st[kW];
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        st[w] = sbuf[w * RP + 32 * mq + lrow];
+        M = fmaxf(M, st[w].x);
+    }
+    float al[kW], Ls = 0.0f, Zs = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        al[w] = (st[w].x == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(st[w].x - M);
+        Ls = __builtin_fmaf(al[w], st[w].y, Ls);
+        Zs = __builtin_fmaf(al[w], st[w].z, Zs);
+    }
+    const float inv = (Ls != 0.0f) ? 1.0f / Ls : 0.0f;
+    const float zo = Zs * inv;
+    float O[4][4]; // [j][dt]: row 32 mq + lrow, coordinate 4 (8 aa + 4h + j) + dt
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            O[j][dt] = zo;
+    // normalised output O = (sum_w al_w acc_w * 2^24 (even d) or 2^20 (odd
+    // d) + Zs) / Ls: the value operand carried c * 2^-24 (even d) and
+    // 16c * 2^-24 (odd d)
+    auto gather = [&](int wbase) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float k = al[wbase + w] * (((dt & 1) ? 1048576.0f : 16777216.0f) * inv);
+                const float4 x = xbuf[(((w * NQT + mq) * 4 + aa) * 4 + dt) * 64 + lane];
+                O[0][dt] = __builtin_fmaf(k, x.x, O[0][dt]);
+                O[1][dt] = __builtin_fmaf(k, x.y, O[1][dt]);
+                O[2][dt] = __builtin_fmaf(k, x.z, O[2][dt]);
+                O[3][dt] = __builtin_fmaf(k, x.w, O[3][dt]);
+            }
+        }
+    };
+    gather(4);
+    __syncthreads();
+    if (wave < 4)
+        put_acc();
+    __syncthreads();
+    gather(0);
+
+    // ------------------------------------------- output or partial state
+    constexpr int kOStride = kD + 4;
+    auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
+    if (a.nsplit > 1 && aa == 0 && h == 0 && tile0 + mq < a.nrt) {
+        float *pm = reinterpret_cast<float *>(&a.part_ml[part_slot(tile0 + mq) + lrow]);
+        __builtin_nontemporal_store(M, pm);
+        __builtin_nontemporal_store(Ls, pm + 1);
+    }
+    if (a.nsplit == 1 && Ls == 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                O[j][k] = __builtin_nanf("");
+    }
+    __syncthreads(); // every wavefront has read the merge buffer
+    float *ob = reinterpret_cast<float *>(lds); // [RP rows][kOStride]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(ob + (32 * mq + lrow) * kOStride + 4 * (8 * aa + 4 * h + j)) =
+            make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
+    __syncthreads();
+    if (a.nsplit == 1) {
+#pragma unroll
+        for (int k = 0; k < RP * kD / 4 / 512; ++k) {
+            const int f4 = threadIdx.x + 512 * k;
+            const int r = f4 >> 5, c = (f4 & 31) * 4;
+            const int grow = row0 + r;
+            if (grow >= Rb)
+                continue;
+            const int n = row_token(grow), g = grow - n * a.G;
+            float *dst = a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD;
+            *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < RP * kD / 8 / 512; ++k) {
+            const int e8 = threadIdx.x + 512 * k;
+            const int r = e8 >> 4, c = (e8 & 15) * 8;
+            if (tile0 + (r >> 5) >= a.nrt)
+                continue;
+            _Float16 *pbase_o = a.part_o + (part_slot(tile0 + (r >> 5)) + (r & 31)) * kD;
+            const float4 x0 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
+            const float4 x1 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float p = fminf(fmaxf(xs[2 * q], -65504.0f), 65504.0f);
+                float r2 = fminf(fmaxf(xs[2 * q + 1], -65504.0f), 65504.0f);
+                p = (xs[2 * q] == xs[2 * q]) ? p : xs[2 * q];
+                r2 = (xs[2 * q + 1] == xs[2 * q + 1]) ? r2 : xs[2 * q + 1];
+                w[q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
+            }
+            __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(pbase_o + c));
+        }
+    }
+}
+
+// Merge of the key ranges of each (b, hk, row tile): out = sum_s w_s O_s /
+// sum_s w_s with w_s = exp2(m_s - max_s m_s) * l_s.  A row is merged by GPR
+// groups of 32 lanes (one float4 of the row per lane), group j taking the
+// j-th contiguous share of the ranges; every lane loads its share's (m, l)
+// pairs and partial float4s in one batch (chunks of kCombineChunk), so
+// the kernel costs one round trip to memory, and the groups' states are
+// then merged through LDS in group order (a fixed order).  Ranges whose
+// softmax sum is exactly 0 saw no token and get weight 0; a NaN sum reaches
+// the output.  Blocks are dealt to the XCDs like the verify work-groups of
+// the same rows, so the partial states are read where they were written.
+// GPR grows with the range count (at most 8 ranges per group up to 64
+// ranges): with one group per row, 64 ranges took four round trips.
+constexpr int kCombineChunk = 8;
+
+template <int GPR> __global__ __launch_bounds__(256) void combine_kernel(VerifyArgs a)
+{
+    constexpr int RPB = 8 / GPR; // rows per block
+    constexpr int kBlocksPerTile = 32 / RPB;
     int blk = blockIdx.x;
     if ((gridDim.x & 7) == 0)
         blk = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const int grp = blk / kBlocksPerTile; // (unit, row tile)
-    const int lrow = (blk % kBlocksPerTile) * kCombineRows + (threadIdx.x >> 5); // row within the tile
+    const int gid = threadIdx.x >> 5, part = gid % GPR;
+    const int lrow = (blk % kBlocksPerTile) * RPB + gid / GPR; // row within the tile
     const int unit = grp / a.nrt, rt = grp % a.nrt;
     const int row = 32 * rt + lrow;
-    if (unit >= a.B * a.Hk)
-        return;
     const int b = unit / a.Hk, hk = unit % a.Hk;
     int nq = a.N, qt0 = b, qts = a.B;
     if (a.cu_q) {
@@ -1387,21 +2046,22 @@ __global__ __launch_bounds__(32 * kCombineRows) void combine_kernel(VerifyArgs a
         nq = min(max(a.cu_q[b + 1] - qt0, 0), a.N);
         qts = 1;
     }
-    if (row >= a.G * nq)
-        return;
+    const bool valid = unit < a.B * a.Hk && row < a.G * nq;
     const int d = (threadIdx.x & 31) * 4;
     const size_t base = (size_t)grp * a.nsplit * 32 + lrow;
+    const int spg = (a.nsplit + GPR - 1) / GPR;
+    const int s_begin = min(part * spg, a.nsplit), s_end = valid ? min(s_begin + spg, a.nsplit) : s_begin;
     float M = -__builtin_inff(), den = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < a.nsplit; s0 += kCombineChunk) {
+    for (int s0 = s_begin; s0 < s_end; s0 += kCombineChunk) {
         float2 ml[kCombineChunk];
         float4 v[kCombineChunk];
         // every load of the chunk is issued before any is used (ranges past
-        // the last re-read the last one and get weight 0): a guarded load
+        // the share re-read its last one and get weight 0): a guarded load
         // per range would cost one memory round trip each
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j) {
-            const size_t ix = base + (size_t)min(s0 + j, a.nsplit - 1) * 32;
+            const size_t ix = base + (size_t)min(s0 + j, s_end - 1) * 32;
             ml[j] = a.part_ml[ix];
             const uint2 hv = *reinterpret_cast<const uint2 *>(a.part_o + ix * kD + d);
             const half2_t h0 = __builtin_bit_cast(half2_t, hv.x), h1 = __builtin_bit_cast(half2_t, hv.y);
@@ -1409,7 +2069,7 @@ __global__ __launch_bounds__(32 * kCombineRows) void combine_kernel(VerifyArgs a
         }
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j)
-            if (s0 + j >= a.nsplit)
+            if (s0 + j >= s_end)
                 ml[j] = make_float2(-__builtin_inff(), 0.0f);
         float Mc = M;
 #pragma unroll
@@ -1434,6 +2094,38 @@ __global__ __launch_bounds__(32 * kCombineRows) void combine_kernel(VerifyArgs a
             acc.w = __builtin_fmaf(w, v[j].w, acc.w);
         }
     }
+    if constexpr (GPR > 1) {
+        // the groups of a row: (M, den, acc) through LDS, merged by group 0
+        __shared__ float4 sacc[8][32];
+        __shared__ float2 smd[8][32];
+        sacc[gid][threadIdx.x & 31] = acc;
+        smd[gid][threadIdx.x & 31] = make_float2(M, den);
+        __syncthreads();
+        if (part != 0)
+            return;
+        float2 st[GPR];
+        float Mt = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < GPR; ++j) {
+            st[j] = smd[gid + j][threadIdx.x & 31];
+            if (st[j].y != 0.0f)
+                Mt = fmaxf(Mt, st[j].x);
+        }
+        den = 0.0f;
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < GPR; ++j) {
+            const float w = (st[j].y != 0.0f) ? __builtin_amdgcn_exp2f(st[j].x - Mt) : 0.0f;
+            const float4 x = sacc[gid + j][threadIdx.x & 31];
+            den = __builtin_fmaf(w, st[j].y, den);
+            acc.x = __builtin_fmaf(w, x.x, acc.x);
+            acc.y = __builtin_fmaf(w, x.y, acc.y);
+            acc.z = __builtin_fmaf(w, x.z, acc.z);
+            acc.w = __builtin_fmaf(w, x.w, acc.w);
+        }
+    }
+    if (!valid)
+        return;
     const float inv = (den != 0.0f) ? 1.0f / den : __builtin_nanf("");
     const int n = (int)(((float)row + 0.5f) * __builtin_amdgcn_rcpf((float)a.G)), g = row - n * a.G;
     *reinterpret_cast<float4 *>(a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD + d) =
@@ -1442,6 +2134,28 @@ __global__ __launch_bounds__(32 * kCombineRows) void combine_kernel(VerifyArgs a
 
 
 
+
+void launch_verify_wide(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
+{
+    const int nwt = (a.nrt + 1) / 2;
+    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * nwt)), block(512);
+    if (preset == kPresetK3V4) {
+        if (paged)
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK3V4, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK3V4, false>), grid, block, 0, s, a);
+    } else if (preset == kPresetK4V4) {
+        if (paged)
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK4V4, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK4V4, false>), grid, block, 0, s, a);
+    } else {
+        if (paged)
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK8V4, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK8V4, false>), grid, block, 0, s, a);
+    }
+}
 
 template <int NQT, bool TR>
 void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
@@ -1475,7 +2189,7 @@ void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t
 hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const VerifyArgs &a, hipStream_t s)
 {
     if (nqt == 2)
-        launch_verify_rows<2, false>(preset, paged, a, s);
+        launch_verify_wide(preset, paged, a, s);
     else if (transposed && a.R <= 8)
         launch_verify_rows<1, true>(preset, paged, a, s);
     else
@@ -1483,9 +2197,17 @@ hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const
     if (hipGetLastError() != hipSuccess)
         return hipErrorLaunchFailure;
     if (a.nsplit > 1) {
-        // 32 / kCombineRows blocks per (unit, row tile)
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hk * a.nrt * (32 / kCombineRows))),
-                           dim3(32 * kCombineRows), 0, s, a);
+        // 4 GPR blocks of 256 threads per (unit, row tile)
+        const int gpr = combine_groups_per_row(a.nsplit);
+        const dim3 grid((unsigned)(a.B * a.Hk * a.nrt * 4 * gpr)), block(256);
+        if (gpr == 1)
+            hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, s, a);
+        else if (gpr == 2)
+            hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, a);
+        else if (gpr == 4)
+            hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, a);
         return hipGetLastError();
     }
     return hipSuccess;
