@@ -275,9 +275,10 @@ def _ws_bytes(cache, n_spec, Hq, num_splits):
     return tqkv_verify_workspace_bytes(cache, n_spec, Hq, num_splits)
 
 
-def _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, workspace, cu_q=None):
+def _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, workspace, cu_q=None, ws_needed=True):
     """Argument checks and defaults shared by the verify calls (dense Q
-    [n_spec, B, Hq, 128], or ragged Q [cu_q[B], Hq, 128] when cu_q is given)."""
+    [n_spec, B, Hq, 128], or ragged Q [cu_q[B], Hq, 128] when cu_q is given;
+    ws_needed False: the call takes no workspace)."""
     if Q.dtype == torch.float32:
         qd = Q_F32
     elif Q.dtype == torch.float16:
@@ -298,15 +299,25 @@ def _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, workspace, cu_
             raise ValueError("cu_q must be on Q's device")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (cache.B,) or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    dev = cache.buffer.device
     if out is None:
-        out = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+        out = torch.empty(Q.shape, dtype=torch.float32, device=dev)
     if out.dtype != torch.float32 or out.shape != Q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor shaped like Q")
+    # every buffer the kernels touch lives on the cache's device (a pointer
+    # of another device, or of host memory, would be read by the kernels)
+    for name, x in (("Q", Q), ("seq_lens", seq_lens), ("out", out), ("cu_q", cu_q), ("workspace", workspace)):
+        if x is not None and x.device != dev:
+            raise ValueError("%s must be on the cache's device (%s), not %s" % (name, dev, x.device))
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if ws_needed is False:
+        return qd, out, None, 0
     need = _ws_bytes(cache, n_spec, Hq, num_splits)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_len = workspace.numel() if workspace is not None else 0
     return qd, out, ws_ptr, ws_len
 
 

@@ -4,6 +4,7 @@
 #include "common.h"
 #include "tqkv.h"
 
+#include <atomic>
 #include <math.h>
 #include <string.h>
 
@@ -11,8 +12,11 @@ namespace {
 
 using namespace tqkv;
 
+// Per-device state, looked up once per device and kept for the process:
+// the compute-unit count, a plain value that any thread may compute again;
+// atomics make concurrent first calls race-free.
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];   // 0 = not probed yet, -1 = not a gfx950 device
+std::atomic<int> g_cu_count[kMaxDevices]; // 0 = not probed yet, -1 = not a gfx950 device
 
 // Number of compute units of the current device, or a negative status when
 // no gfx950 device is current.
@@ -21,14 +25,16 @@ int current_device_cus()
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return TQKV_ERR_DEVICE;
-    if (g_cu_count[dev] == 0) {
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return TQKV_ERR_DEVICE;
         const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        g_cu_count[dev] = ok ? prop.multiProcessorCount : -1;
+        n = ok ? prop.multiProcessorCount : -1;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
     }
-    return g_cu_count[dev] > 0 ? g_cu_count[dev] : TQKV_ERR_DEVICE;
+    return n > 0 ? n : TQKV_ERR_DEVICE;
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }

@@ -241,3 +241,35 @@ def test_varlen_rejects_bad_arguments():
     assert call(mq=129) == -2
     assert call(cu=4098) == -3
     assert call(Q=4100) == -3
+
+
+def test_binding_rejects_buffers_off_the_cache_device():
+    """Every tensor a verify call hands to the kernels must live on the
+    cache's device; the binding refuses others before calling the library
+    (a CPU cache and meta tensors stand in for two devices here)."""
+    import torch
+    cache = tq.Cache(tq.K8V4, 1, 1, 64, device="cpu")
+    N, Hq = 8, 8
+    Q = torch.zeros(N, 1, Hq, 128)
+    sl = torch.full((1,), 64, dtype=torch.int32)
+    out = torch.zeros(N, 1, Hq, 128)
+    meta = dict(device="meta")
+    cases = [
+        dict(Q=torch.zeros(N, 1, Hq, 128, **meta)),
+        dict(seq_lens=torch.zeros(1, dtype=torch.int32, **meta)),
+        dict(out=torch.zeros(N, 1, Hq, 128, **meta)),
+        dict(workspace=torch.zeros(64, dtype=torch.uint8, **meta)),
+    ]
+    for c in cases:
+        args = dict(Q=Q, seq_lens=sl, out=out, workspace=None)
+        args.update(c)
+        name = next(iter(c))
+        with pytest.raises(ValueError, match="%s must be on the cache's device" % name):
+            tq.tqkv_verify(cache, args["Q"], args["seq_lens"], N, Hq, True, out=args["out"],
+                           workspace=args["workspace"])
+    cu = torch.tensor([0, N], dtype=torch.int32, device="meta")
+    with pytest.raises(ValueError, match="must be on"):
+        tq.tqkv_verify_varlen(cache, Q.reshape(N, Hq, 128), cu, N, sl, Hq, True)
+    for ws in (torch.zeros(16, dtype=torch.float32), torch.zeros(64, dtype=torch.uint8)[::2]):
+        with pytest.raises(ValueError, match="workspace must be a contiguous uint8"):
+            tq.tqkv_verify(cache, Q, sl, N, Hq, True, out=out, workspace=ws)
