@@ -20,7 +20,10 @@
  * nothing between host and device, and never synchronises: each call
  * enqueues its kernels on `stream` (a hipStream_t; NULL = the default
  * stream) and returns.  Calls are reentrant; the library keeps no state
- * besides read-only constant tables.
+ * besides read-only constant tables, the per-device values it looks up once
+ * (compute-unit count) and the scratch array of tqkv_verify_noalloc (a
+ * static device array of TQKV_NOALLOC_SCRATCH_BYTES per device, which only
+ * that call uses).
  *
  * Errors.  Every entry point validates its host-side arguments first and
  * returns a negative tqkv_status without launching anything when they are
@@ -67,6 +70,7 @@ extern "C" {
 #define TQKV_MAX_QLEN 128    /* queries per sequence (n_spec, or the largest ragged count) */
 #define TQKV_MAX_ROWS 8192   /* (Hq / Hk) * queries per sequence must not exceed this */
 #define TQKV_MAX_PAGES_PER_SEQ 524288 /* block-table row length of a paged cache (8M tokens) */
+#define TQKV_NOALLOC_SCRATCH_BYTES (8u << 20) /* workspace held by the library per device for tqkv_verify_noalloc */
 
 typedef enum {
     TQKV_K8V4 = 1,    /* FP8 E4M3 keys with a per-token fp16 scale, 4-bit values */
@@ -194,6 +198,26 @@ int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int
 int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens,
                 int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* tqkv_verify for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, result, preconditions and errors as tqkv_verify, but
+ * the workspace is the library's own scratch array of
+ * TQKV_NOALLOC_SCRATCH_BYTES per device (a static device array, created
+ * when the library's code is loaded on a device and held until the process
+ * ends).  The call allocates and frees nothing.  A shape whose
+ * tqkv_verify_workspace_bytes exceeds TQKV_NOALLOC_SCRATCH_BYTES returns
+ * TQKV_ERR_WORKSPACE without launching (with 64 query rows per KV head
+ * every (b, hk, key range) takes 16896 bytes: 8 MiB holds
+ * B * Hk * splits <= 496, e.g. the PoC shape's 16 * 16).  Every call on a device shares that
+ * device's array and nothing in it needs clearing (each call writes the
+ * partial states before it reads them); calls that may overlap on one device
+ * (several streams, several host threads) race on it and must be ordered
+ * by the caller, e.g. issued on one stream.
+ * Returns TQKV_OK or a negative tqkv_status. */
+int tqkv_verify_noalloc(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens,
+                        int n_spec, int Hq, int causal, int num_splits, float sm_scale, float *out,
+                        void *stream);
 
 /* tqkv_verify with a different number of queries per sequence, packed (the
  * verify of per-sequence draft lengths, or a continuation chunk of up to

@@ -15,6 +15,7 @@ Names mirror the C entry points::
     tqkv_verify_num_splits(cache, n_spec, Hq, num_splits)
     tqkv_verify_workspace_bytes(cache, n_spec, Hq, num_splits)
     tqkv_verify(cache, Q, seq_lens, n_spec, Hq, causal, ...)
+    tqkv_verify_noalloc(cache, Q, seq_lens, n_spec, Hq, causal, ...)
     tqkv_store_verify(cache, K, V, Q, seq_lens, n_spec, Hq, causal, ...)
     tqkv_verify_varlen(cache, Q, cu_q, max_q, seq_lens, Hq, causal, ...)
     tqkv_paged_cache_bytes(preset, Hk, D, num_pages)
@@ -38,7 +39,8 @@ import torch
 __all__ = [
     "K8V4", "K3V4_NC", "K4V4_NC", "HEAD_DIM", "BLOCK_TOKENS", "MAX_QLEN", "TqkvError", "Cache", "PagedCache",
     "library_path", "tqkv_slot_bytes", "tqkv_block_bytes", "tqkv_cache_bytes", "tqkv_store",
-    "tqkv_verify_num_splits", "tqkv_verify_workspace_bytes", "tqkv_verify", "tqkv_store_verify",
+    "tqkv_verify_num_splits", "tqkv_verify_workspace_bytes", "tqkv_verify", "tqkv_verify_noalloc",
+    "tqkv_store_verify", "NOALLOC_SCRATCH_BYTES",
     "tqkv_verify_varlen", "tqkv_paged_cache_bytes", "tqkv_paged_store", "tqkv_paged_verify_num_splits",
     "tqkv_paged_verify_workspace_bytes", "tqkv_paged_verify", "tqkv_paged_verify_varlen",
     "tqkv_paged_store_verify", "tqkv_status_string", "tqkv_version",
@@ -50,6 +52,7 @@ K4V4_NC = 3
 HEAD_DIM = 128
 BLOCK_TOKENS = 16
 MAX_QLEN = 128
+NOALLOC_SCRATCH_BYTES = 8 << 20
 Q_F32 = 0
 Q_F16 = 1
 
@@ -103,6 +106,8 @@ def _load():
     L.tqkv_verify_workspace_bytes.restype = I
     L.tqkv_verify.argtypes = [D, P, I, P, I, I, I, I, ctypes.c_float, P, P, S, P]
     L.tqkv_verify.restype = I
+    L.tqkv_verify_noalloc.argtypes = [D, P, I, P, I, I, I, I, ctypes.c_float, P, P]
+    L.tqkv_verify_noalloc.restype = I
     L.tqkv_store_verify.argtypes = [D, P, P, P, I, P, I, I, I, I, ctypes.c_float, P, P, S, P]
     L.tqkv_store_verify.restype = I
     PD = ctypes.POINTER(_PagedDesc)
@@ -334,6 +339,26 @@ def tqkv_verify(cache: Cache, Q: torch.Tensor, seq_lens: torch.Tensor, n_spec: i
                              Hq, int(bool(causal)), num_splits, float(sm_scale), out.data_ptr(),
                              ws_ptr, ws_len, _stream_ptr(Q, stream))
     _check(st, "tqkv_verify")
+    return out
+
+
+def tqkv_verify_noalloc(cache: Cache, Q: torch.Tensor, seq_lens: torch.Tensor, n_spec: int, Hq: int,
+                        causal: bool, num_splits: int = 0, sm_scale: float = 0.0,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """tqkv_verify with the library's own per-device scratch array as the
+    workspace: nothing is allocated (``out`` is required).  Raises
+    TqkvError(TQKV_ERR_WORKSPACE) when the shape needs more than
+    NOALLOC_SCRATCH_BYTES; calls that overlap on one device race on the
+    array (issue them on one stream)."""
+    if not isinstance(cache, Cache):
+        raise TypeError("tqkv_verify_noalloc takes a contiguous Cache")
+    if out is None:
+        raise ValueError("tqkv_verify_noalloc needs a caller-provided out tensor")
+    qd, out, _, _ = _verify_prep(cache, Q, seq_lens, n_spec, Hq, num_splits, out, None, ws_needed=False)
+    st = _load().tqkv_verify_noalloc(ctypes.byref(cache.desc), Q.data_ptr(), qd, seq_lens.data_ptr(), n_spec,
+                                     Hq, int(bool(causal)), num_splits, float(sm_scale), out.data_ptr(),
+                                     _stream_ptr(Q, stream))
+    _check(st, "tqkv_verify_noalloc")
     return out
 
 

@@ -13,10 +13,20 @@ namespace {
 using namespace tqkv;
 
 // Per-device state, looked up once per device and kept for the process:
-// the compute-unit count, a plain value that any thread may compute again;
-// atomics make concurrent first calls race-free.
+// the compute-unit count and the device address of the scratch array of
+// tqkv_verify_noalloc.  Both are plain values that any thread may compute
+// again; atomics make the concurrent first calls race-free.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices]; // 0 = not probed yet, -1 = not a gfx950 device
+std::atomic<void *> g_scratch[kMaxDevices]; // null = not looked up yet
+
+// The workspace of tqkv_verify_noalloc: one array per device, allocated
+// when the code object is loaded on that device and held until the process
+// ends.  Host code never uses its name as an address (on the host it is a
+// stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = TQKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 // Number of compute units of the current device, or a negative status when
 // no gfx950 device is current.
@@ -35,6 +45,24 @@ int current_device_cus()
         g_cu_count[dev].store(n, std::memory_order_relaxed);
     }
     return n > 0 ? n : TQKV_ERR_DEVICE;
+}
+
+// Device address of the current device's scratch array (looked up on the
+// first call on each device, with that device current), or a negative
+// status.
+int current_device_scratch(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TQKV_ERR_DEVICE;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return TQKV_ERR_DEVICE;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return TQKV_OK;
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -451,6 +479,24 @@ int tqkv_verify(const tqkv_cache *cache, const void *Q, int q_dtype, const int32
         return st;
     return verify_impl(v, nullptr, nullptr, Q, q_dtype, nullptr, seq_lens, n_spec, Hq, causal, num_splits, sm_scale,
                        out, workspace, workspace_bytes, stream);
+}
+
+int tqkv_verify_noalloc(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *seq_lens, int n_spec,
+                        int Hq, int causal, int num_splits, float sm_scale, float *out, void *stream)
+{
+    View v;
+    int st = view_of(cache, v);
+    if (st != TQKV_OK)
+        return st;
+    // the partial states go to the library's scratch array: a shape that
+    // needs more than it holds is refused (TQKV_ERR_WORKSPACE, from
+    // verify_impl's size check) before anything is launched
+    void *ws = nullptr;
+    st = current_device_scratch(&ws);
+    if (st != TQKV_OK)
+        return st;
+    return verify_impl(v, nullptr, nullptr, Q, q_dtype, nullptr, seq_lens, n_spec, Hq, causal, num_splits, sm_scale,
+                       out, ws, kScratchBytes, stream);
 }
 
 int tqkv_verify_varlen(const tqkv_cache *cache, const void *Q, int q_dtype, const int32_t *cu_q, int max_q,

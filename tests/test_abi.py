@@ -243,6 +243,12 @@ def test_varlen_rejects_bad_arguments():
     assert call(Q=4100) == -3
 
 
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "tqkv.h")).read()
+    m = re.search(r"#define\s+TQKV_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == tq.NOALLOC_SCRATCH_BYTES
+
+
 def test_binding_rejects_buffers_off_the_cache_device():
     """Every tensor a verify call hands to the kernels must live on the
     cache's device; the binding refuses others before calling the library
@@ -273,3 +279,7 @@ def test_binding_rejects_buffers_off_the_cache_device():
     for ws in (torch.zeros(16, dtype=torch.float32), torch.zeros(64, dtype=torch.uint8)[::2]):
         with pytest.raises(ValueError, match="workspace must be a contiguous uint8"):
             tq.tqkv_verify(cache, Q, sl, N, Hq, True, out=out, workspace=ws)
+    with pytest.raises(ValueError, match="needs a caller-provided out"):
+        tq.tqkv_verify_noalloc(cache, Q, sl, N, Hq, True)
+    with pytest.raises(ValueError, match="out must be on"):
+        tq.tqkv_verify_noalloc(cache, Q, sl, N, Hq, True, out=torch.zeros(N, 1, Hq, 128, **meta))
