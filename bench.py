@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--kernel-calls", type=int, default=200,
                     help="back-to-back verify calls for the per-launch kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-nested", action="store_true",
+                    help="time only --workload (not the other workloads' nested entries)")
     ap.add_argument("--replay-check", action="store_true",
                     help="replay the timed graph a second time and print its duration (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -112,6 +114,217 @@ def copy_reference(mb):
     print(json.dumps({"copy_reference_bytes": n, "copies": 20}))
 
 
+ALL_WORKLOADS = ("poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc", "long_k3v4_nc", "decode_k3v4_nc")
+PRESET_NAME = {1: "k8v4", 2: "k3v4_nc", 3: "k4v4_nc"}
+
+
+def workload_label(name, cfg):
+    return "%s: preset=%s N_spec=%d B=%d Hq=%d Hk=%d D=128 seqlen=%d causal=%s" % (
+        name, PRESET_NAME[cfg["preset"]], cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"], cfg["causal"])
+
+
+def capture(fn, n, offset=0):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(offset + i)
+    return g
+
+
+def time_graph(g):
+    """Duration (ms) of one replay, HIP events on the launch stream."""
+    import torch
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def median5(g, n):
+    """Per-call ms of a graph of n calls: median of 5 replays."""
+    return statistics.median(time_graph(g) for _ in range(5)) / n
+
+
+class Workload:
+    """Device-resident inputs of one workload: R byte-identical cache
+    replicas (R * bytes >= cold_mb), a paged pool with its replicas (primary
+    only), the queries, the N_spec new tokens of the step and the outputs.
+
+    host=True: the inputs of tests/synth.py (the host generator the parity
+    tests use); host=False: the same distributions drawn on the device with
+    torch's seeded generator (the decode inputs take about a minute on the
+    host), the cache filled by one bulk tqkv_store call of every token."""
+
+    def __init__(self, name, args, dev, host, paged):
+        import torch
+
+        import quantized_kv_attention_amd as tq
+        from tests import synth
+        from tests.gputil import gpu_paged_store_all, gpu_store_all, page_table, to_dev
+
+        self.name, self.dev = name, dev
+        cfg = self.cfg = synth.config(name)
+        N, B, Hq, Hk, S = cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"]
+        self.preset = cfg["preset"]
+        print("bench: workload %s, generating inputs" % name, file=sys.stderr, flush=True)
+        if host:
+            inp = synth.make_inputs(cfg)
+            base = gpu_store_all(cfg, inp, device=dev)
+            self.Q = to_dev(inp["Q"], dev)
+            # the step's N new tokens of every sequence as [N, B, Hk, 128]
+            self.Kf = to_dev(np.ascontiguousarray(inp["K"][:, S - N:S].transpose(1, 0, 2, 3)), dev)
+            self.Vf = to_dev(np.ascontiguousarray(inp["V"][:, S - N:S].transpose(1, 0, 2, 3)), dev)
+            self.host_inputs = inp
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(cfg["seed"])
+            self.Q = torch.randn((N, B, Hq, 128), generator=g, device=dev, dtype=torch.float32)
+            K = torch.randn((B, S, Hk, 128), generator=g, device=dev, dtype=torch.float16)
+            V = torch.randn((B, S, Hk, 128), generator=g, device=dev, dtype=torch.float16)
+            base = tq.Cache(self.preset, B, Hk, S, device=dev)
+            si = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(S)
+            po = torch.arange(S, dtype=torch.int32, device=dev).repeat(B)
+            tq.tqkv_store(base, K.view(B * S, Hk, 128), V.view(B * S, Hk, 128), si, po)
+            self.Kf = K[:, S - N:S].transpose(0, 1).contiguous()
+            self.Vf = V[:, S - N:S].transpose(0, 1).contiguous()
+            self.host_inputs = None
+            self.bulk = (K.view(B * S, Hk, 128), V.view(B * S, Hk, 128), si, po)
+        self.sl = torch.full((B,), S, dtype=torch.int32, device=dev)
+        self.nbytes = base.nbytes
+        self.R = max(1, int(math.ceil(args.cold_mb * 2 ** 20 / self.nbytes)))
+        self.caches = [base] + [tq.Cache(self.preset, B, Hk, S, device=dev, buffer=base.buffer.clone())
+                                for _ in range(self.R - 1)]
+        self.pools = None
+        if paged:
+            table = page_table(B, S)
+            pbase = gpu_paged_store_all(cfg, self.host_inputs, table, device=dev)
+            self.pools = [pbase] + [tq.PagedCache(self.preset, Hk, pbase.num_pages, device=dev,
+                                                  buffer=pbase.buffer.clone(), block_table=pbase.block_table)
+                                    for _ in range(self.R - 1)]
+        self.out = torch.empty((N, B, Hq, 128), dtype=torch.float32, device=dev)
+        ws = 16
+        for ns in (args.num_splits, 8):
+            ws = max(ws, tq.tqkv_verify_workspace_bytes(base, N, Hq, ns))
+            if paged:
+                ws = max(ws, tq.tqkv_paged_verify_workspace_bytes(self.pools[0], N, Hq, ns))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def verify(self, i, ns):
+        import quantized_kv_attention_amd as tq
+        c = self.cfg
+        tq.tqkv_verify(self.caches[i % self.R], self.Q, self.sl, c["N"], c["Hq"], c["causal"], num_splits=ns,
+                       out=self.out, workspace=self.ws)
+
+    def step(self, i, ns):
+        import quantized_kv_attention_amd as tq
+        c = self.cfg
+        tq.tqkv_store_verify(self.caches[i % self.R], self.Kf, self.Vf, self.Q, self.sl, c["N"], c["Hq"],
+                             c["causal"], num_splits=ns, out=self.out, workspace=self.ws)
+
+    def verify_paged(self, i, ns):
+        import quantized_kv_attention_amd as tq
+        c = self.cfg
+        tq.tqkv_paged_verify(self.pools[i % self.R], self.Q, self.sl, c["N"], c["Hq"], c["causal"],
+                             num_splits=ns, out=self.out, workspace=self.ws)
+
+    def step_paged(self, i, ns):
+        import quantized_kv_attention_amd as tq
+        c = self.cfg
+        tq.tqkv_paged_store_verify(self.pools[i % self.R], self.Kf, self.Vf, self.Q, self.sl, c["N"], c["Hq"],
+                                   c["causal"], num_splits=ns, out=self.out, workspace=self.ws)
+
+    def store_bulk_us(self, calls):
+        """Per-call us of a bulk tqkv_store of every token of the workload
+        (all B * S tokens, all KV heads) into a scratch cache."""
+        import torch
+
+        import quantized_kv_attention_amd as tq
+        from tests import synth
+        from tests.gputil import to_dev
+        c = self.cfg
+        B, S, Hk = c["B"], c["S"], c["Hk"]
+        if self.host_inputs is not None:
+            si, po = synth.token_lists(B, S)
+            K = to_dev(synth.rows(self.host_inputs["K"]), self.dev)
+            V = to_dev(synth.rows(self.host_inputs["V"]), self.dev)
+            si, po = to_dev(si, self.dev), to_dev(po, self.dev)
+        else:
+            K, V, si, po = self.bulk
+        dst = tq.Cache(self.preset, B, Hk, S, device=self.dev)
+        tq.tqkv_store(dst, K, V, si, po)
+        g = capture(lambda i: tq.tqkv_store(dst, K, V, si, po), calls)
+        us = median5(g, calls) * 1e3
+        del g, dst
+        torch.cuda.empty_cache()
+        return us
+
+    def release(self):
+        import torch
+        self.caches = self.pools = self.bulk = self.host_inputs = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def verify_entry(w, args):
+    """us per call of the verify launch (auto splits and 8 splits), of the
+    fused step, of a bulk store of every token, and the verify roofline."""
+    import quantized_kv_attention_amd as tq
+    c = w.cfg
+    N, B, Hq, Hk, S = c["N"], c["B"], c["Hq"], c["Hk"], c["S"]
+    slot = tq.tqkv_slot_bytes(w.preset)
+    calls = args.kernel_calls
+    ns = args.num_splits
+    # warm the code objects outside the graphs
+    w.verify(0, ns)
+    w.step(0, ns)
+    verify_ms = median5(capture(lambda i: w.verify(i, ns), calls), calls)
+    verify8_ms = median5(capture(lambda i: w.verify(i, 8), calls), calls)
+    step_ms = median5(capture(lambda i: w.step(i, ns), calls), calls)
+    bulk_us = w.store_bulk_us(max(2, calls // 20))
+    kv_bytes = B * S * Hk * slot
+    qo_bytes = 2 * N * B * Hq * 128 * 4
+    achieved = (kv_bytes + qo_bytes) / (verify_ms * 1e-3) / 1e9
+    flops = 4 * N * B * Hq * S * 128
+    tflops = flops / (verify_ms * 1e-3) / 1e12
+    th = B * S * Hk
+    bulk_bytes = th * (2 * 128 * 2 + slot)  # fp16 K and V read, the packed token-head written
+    return {
+        "workload": workload_label(w.name, c),
+        "num_splits": tq.tqkv_verify_num_splits(w.caches[0], N, Hq, ns),
+        "cold_replicas": w.R,
+        "us_per_verify_call": round(verify_ms * 1e3, 3),
+        "us_per_verify_call_splits8": round(verify8_ms * 1e3, 3),
+        "us_per_step": round(step_ms * 1e3, 3),
+        "kv_bytes_per_call": kv_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(w.name),
+            "bytes_per_launch": kv_bytes + qo_bytes,
+            "mfma": {"flops_per_launch": flops, "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        },
+        "store_bulk": {
+            "token_heads": th,
+            "bytes_per_token_head": 2 * 128 * 2 + slot,
+            "us_per_call": round(bulk_us, 3),
+            "achieved": round(bulk_bytes / (bulk_us * 1e-6) / 1e9, 1),
+            "unit": "GB/s",
+            "frac": round(bulk_bytes / (bulk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+    }
+
+
 def main():
     args = parse()
     if args.copy_reference > 0:
@@ -126,103 +339,40 @@ def main():
     import torch
 
     import quantized_kv_attention_amd as tq
-    from tests import synth
-    from tests.gputil import gpu_paged_store_all, gpu_store_all, page_table, to_dev
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = synth.config(args.workload)
+    w = Workload(args.workload, args, dev, host=True, paged=True)
+    cfg = w.cfg
     N, B, Hq, Hk, S = cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"]
-    preset = cfg["preset"]
-    slot = tq.tqkv_slot_bytes(preset)
-    print("bench: workload %s, generating inputs" % args.workload, file=sys.stderr, flush=True)
-    inp = synth.make_inputs(cfg)
-
-    # ---- device-resident inputs
-    base = gpu_store_all(cfg, inp, device=dev)
-    nbytes = base.nbytes
-    R = max(1, int(math.ceil(args.cold_mb * 2 ** 20 / nbytes)))
-    caches = [base]
-    for _ in range(R - 1):
-        caches.append(tq.Cache(preset, B, Hk, S, device=dev, buffer=base.buffer.clone()))
-    # the same tokens in a paged pool (random page order), R replicas
-    table = page_table(B, S)
-    pbase = gpu_paged_store_all(cfg, inp, table, device=dev)
-    pools = [pbase]
-    for _ in range(R - 1):
-        pools.append(tq.PagedCache(preset, Hk, pbase.num_pages, device=dev, buffer=pbase.buffer.clone(),
-                                   block_table=pbase.block_table))
+    slot = tq.tqkv_slot_bytes(w.preset)
+    ns = args.num_splits
+    splits = tq.tqkv_verify_num_splits(w.caches[0], N, Hq, ns)
+    # the step's store alone (N new tokens per sequence), for the unfused pair
+    from tests import synth
+    from tests.gputil import to_dev
     si, po = synth.token_lists(B, S, S - N, S)
-    Kn = to_dev(synth.rows(inp["K"], S - N, S), dev)
-    Vn = to_dev(synth.rows(inp["V"], S - N, S), dev)
-    # the same new tokens as [N, B, Hk, 128] for the fused store + verify call
-    Kf = to_dev(np.ascontiguousarray(inp["K"][:, S - N:S].transpose(1, 0, 2, 3)), dev)
-    Vf = to_dev(np.ascontiguousarray(inp["V"][:, S - N:S].transpose(1, 0, 2, 3)), dev)
+    Kn = to_dev(synth.rows(w.host_inputs["K"], S - N, S), dev)
+    Vn = to_dev(synth.rows(w.host_inputs["V"], S - N, S), dev)
     si_d, po_d = to_dev(si, dev), to_dev(po, dev)
-    Q = to_dev(inp["Q"], dev)
-    sl = to_dev(inp["seq_lens"], dev)
-    out = torch.empty((N, B, Hq, 128), dtype=torch.float32, device=dev)
-    ws_bytes = max(tq.tqkv_verify_workspace_bytes(base, N, Hq, args.num_splits),
-                   tq.tqkv_paged_verify_workspace_bytes(pbase, N, Hq, args.num_splits))
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    splits = tq.tqkv_verify_num_splits(base, N, Hq, args.num_splits)
-    torch.cuda.synchronize()
-    del inp["K"], inp["V"]
 
     def store(i):
-        tq.tqkv_store(caches[i % R], Kn, Vn, si_d, po_d)
-
-    def verify(i):
-        tq.tqkv_verify(caches[i % R], Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
-                       out=out, workspace=ws)
-
-    def step(i):
-        tq.tqkv_store_verify(caches[i % R], Kf, Vf, Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
-                             out=out, workspace=ws)
-
-    def verify_paged(i):
-        tq.tqkv_paged_verify(pools[i % R], Q, sl, N, Hq, cfg["causal"], num_splits=args.num_splits,
-                             out=out, workspace=ws)
-
-    def step_paged(i):
-        tq.tqkv_paged_store_verify(pools[i % R], Kf, Vf, Q, sl, N, Hq, cfg["causal"],
-                                   num_splits=args.num_splits, out=out, workspace=ws)
+        tq.tqkv_store(w.caches[i % w.R], Kn, Vn, si_d, po_d)
 
     def step_unfused(i):
         store(i)
-        verify(i)
-
-    def capture(fn, n, offset=0):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(offset + i)
-        return g
-
-    def time_graph(g):
-        torch.cuda.synchronize()
-        st = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)  # ms
+        w.verify(i, ns)
 
     # ---- eager warmup (also loads the code objects), then graphs
     for i in range(max(1, args.warmup)):
-        step(i)
+        w.step(i, ns)
     torch.cuda.synchronize()
-    print("bench: capturing graphs (R=%d replicas of %.1f MB, splits=%d)" % (R, nbytes / 1e6, splits),
+    print("bench: capturing graphs (R=%d replicas of %.1f MB, splits=%d)" % (w.R, w.nbytes / 1e6, splits),
           file=sys.stderr, flush=True)
-    g_warm = capture(step, max(1, args.warmup))
-    g_steps = capture(step, args.steps)
-    g_verify = capture(verify, args.kernel_calls)
-    g_store = capture(store, args.kernel_calls)
-    g_unfused = capture(step_unfused, args.kernel_calls)
-    g_vpaged = capture(verify_paged, args.kernel_calls)
-    g_spaged = capture(step_paged, args.kernel_calls)
+    g_warm = capture(lambda i: w.step(i, ns), max(1, args.warmup))
+    # the timed steps continue the replica sequence where the warmup stops,
+    # so no timed step starts on a replica the warmup has just touched
+    g_steps = capture(lambda i: w.step(i, ns), args.steps, offset=max(1, args.warmup))
     # the first launch of a graph also copies it to the device; that one-time
     # set-up (like the capture) stays out of the timed region, and the
     # warmup steps run right before it (no idle gap for the clocks to drop)
@@ -244,49 +394,58 @@ def main():
         torch.cuda.synchronize()
         print("bench: second replay %.3f ms" % ((time.perf_counter() - t0) * 1e3), file=sys.stderr, flush=True)
 
-    # the same step graph timed with HIP events (best of 3 replays)
-    def median5(g, n):
-        return statistics.median(time_graph(g) for _ in range(5)) / n
-
+    calls = args.kernel_calls
     step_events_ms = median5(g_steps, args.steps)
+    del g_steps, g_warm
     # per-launch durations with HIP events on the launch stream, median of 5
     # replays of a graph of back-to-back calls
-    verify_ms = median5(g_verify, args.kernel_calls)
-    store_ms = median5(g_store, args.kernel_calls)
-    unfused_ms = median5(g_unfused, args.kernel_calls)
-    vpaged_ms = median5(g_vpaged, args.kernel_calls)
-    spaged_ms = median5(g_spaged, args.kernel_calls)
+    entry = verify_entry(w, args)
+    verify_ms = entry["us_per_verify_call"] * 1e-3
+    store_ms = median5(capture(store, calls), calls)
+    unfused_ms = median5(capture(step_unfused, calls), calls)
+    vpaged_ms = median5(capture(lambda i: w.verify_paged(i, ns), calls), calls)
+    spaged_ms = median5(capture(lambda i: w.step_paged(i, ns), calls), calls)
     # warm (MALL-resident) verify: one replica only
-    g_warmv = capture(lambda i: verify(0), args.kernel_calls)
-    verify_warm_ms = median5(g_warmv, args.kernel_calls)
+    verify_warm_ms = median5(capture(lambda i: w.verify(0, ns), calls), calls)
     # what a plain read+write stream reaches on this machine: device copies of
     # 256 MB (bytes moved = 2 x 256 MB per copy), median of 5 graphs of 10
     csrc = torch.empty(256 * 10**6, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
-    g_copy = capture(lambda i: cdst.copy_(csrc), 10)
-    copy_gbs = 2 * csrc.numel() / (median5(g_copy, 10) * 1e-3) / 1e9
-    del g_copy, csrc, cdst
+    copy_gbs = 2 * csrc.numel() / (median5(capture(lambda i: cdst.copy_(csrc), 10), 10) * 1e-3) / 1e9
+    del csrc, cdst
     # eager steps, for reference
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        w.step(i, ns)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    host_inputs = w.host_inputs
+    w.release()
+
+    # ---- the other workloads: verify, step and bulk store, nested
+    nested = {}
+    if not args.no_nested:
+        for name in ALL_WORKLOADS:
+            if name == args.workload:
+                continue
+            wn = Workload(name, args, dev, host=False, paged=False)
+            nested[name] = verify_entry(wn, args)
+            wn.release()
+            del wn
 
     kv_bytes = B * S * Hk * slot
-    qo_bytes = 2 * N * B * Hq * 128 * 4
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = (kv_bytes + qo_bytes) / (verify_ms * 1e-3) / 1e9
-    # the two fp16 contractions Q K^T and P V: 2 FLOPs per (row, token, d) each
-    flops = 4 * N * B * Hq * S * 128
-    tflops = flops / (verify_ms * 1e-3) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, host_inputs, args.cpu_seconds)
 
     pages_ms = PAGES_FUSED_TRITON_MS.get(args.workload)
+    roof = dict(entry["roofline"])
+    roof["kernel"] = "tqkv_verify: verify_wide_kernel (+ combine_kernel when splits > 1)"
+    roof["measured_copy_GBps"] = round(copy_gbs, 1)
+    roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
     rec = {
         "metric": "verify-attention µs/call + effective KV GB/s (frac of HBM peak), PoC shape",
         "value": round(value, 2),
@@ -301,17 +460,16 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "%s: preset=%s N_spec=%d B=%d Hq=%d Hk=%d D=128 seqlen=%d causal=%s"
-                        % (args.workload, {1: "k8v4", 2: "k3v4_nc", 3: "k4v4_nc"}[preset], N, B, Hq, Hk, S,
-                           cfg["causal"]),
+            "workload": workload_label(args.workload, cfg),
             "num_splits": splits,
-            "cold_replicas": R,
+            "cold_replicas": w.R,
             "step": "tqkv_store_verify: store(N_spec new tokens x B x Hk) + verify(all tokens), one launch",
             "timing": "HIP graph of K steps, one replay",
         },
         "us_per_step": round(ms_per_step * 1e3, 3),
         "us_per_step_events_median_of_5": round(step_events_ms * 1e3, 3),
-        "us_per_verify_call": round(verify_ms * 1e3, 3),
+        "us_per_verify_call": entry["us_per_verify_call"],
+        "us_per_verify_call_splits8": entry["us_per_verify_call_splits8"],
         "us_per_store_call": round(store_ms * 1e3, 3),
         "us_per_step_store_then_verify": round(unfused_ms * 1e3, 3),
         "us_per_verify_call_mall_warm": round(verify_warm_ms * 1e3, 3),
@@ -319,21 +477,10 @@ def main():
         "us_per_step_paged": round(spaged_ms * 1e3, 3),
         "us_per_step_eager": round(eager_ms * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.workload),
-            "kernel": "tqkv_verify: verify_kernel (+ combine_kernel when splits > 1)",
-            "bytes_per_launch": kv_bytes + qo_bytes,
-            "measured_copy_GBps": round(copy_gbs, 1),
-            "frac_of_measured_copy": round(achieved / copy_gbs, 4),
-            "mfma": {"flops_per_launch": flops, "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
-        },
+        "store_bulk": entry["store_bulk"],
+        "roofline": roof,
         "cpu_baseline": cpu,
+        "workloads": nested,
     }
     if pages_ms:
         rec["context_pages_b70_fused_triton_us"] = pages_ms * 1e3
@@ -356,61 +503,73 @@ def upload_graph(g):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, seconds):
+def _omp_set_threads(n):
+    """Thread count of the oracle's OpenMP loops (the runtime libtqoracle.so
+    links is process-wide)."""
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def cpu_baseline(cfg, inp, seconds):
     """The oracle (as it stands) timed on this host's cores on a sample of
-    the same workload: the full step for as many (b, hk) units as fit in
-    about `seconds` of CPU time."""
+    the same workload, with every available thread and with one: one step
+    (store of the N new tokens + verify) for a few (b, hk) units, repeated
+    until about `seconds` have passed in each leg."""
     import oracle
     from tests import synth
 
     cores = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-    threads = int(os.environ["OMP_NUM_THREADS"])
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     N, B, Hq, Hk, S = cfg["N"], cfg["B"], cfg["Hq"], cfg["Hk"], cfg["S"]
     preset = cfg["preset"]
-    inp = synth.make_inputs(cfg)
     slot = oracle.slot_bytes(preset)
-    # sample: the first nb sequences (all of their KV heads), as many as give
-    # every thread a (b, hk) unit -- the oracle's verify, the bulk of the
-    # step, runs one thread per unit; the sequences are stored once outside
-    # the timing, and the timed part is one step (store of their N new
-    # tokens + verify), repeated until `seconds` have passed
-    nb = min(B, max(1, threads // Hk))
-    cache = np.zeros(oracle.cache_bytes(preset, nb, Hk, S), np.uint8)
-    si, po = synth.token_lists(nb, S)
-    oracle.store(preset, cache, nb, Hk, S, synth.rows(inp["K"][:nb]), synth.rows(inp["V"][:nb]), si, po)
-    si_n, po_n = synth.token_lists(nb, S, S - N, S)
-    Kn = synth.rows(inp["K"][:nb], S - N, S)
-    Vn = synth.rows(inp["V"][:nb], S - N, S)
-    Q = np.ascontiguousarray(inp["Q"][:, :nb])
-    sl = inp["seq_lens"][:nb]
-    reps, t_total = 0, 0.0
-    while t_total < seconds or reps == 0:
-        t0 = time.perf_counter()
-        oracle.store(preset, cache, nb, Hk, S, Kn, Vn, si_n, po_n)
-        oracle.verify(preset, cache, nb, Hk, S, Q, sl, Hq, cfg["causal"])
-        t_total += time.perf_counter() - t0
-        reps += 1
-    per_step = t_total / reps
-    kv = nb * S * Hk * slot
-    used = min(threads, nb * Hk)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {
-        "value": round(kv / per_step / 1e9, 4),
-        "unit": "GB/s",
-        "cores": used,
-        "threads_available": threads,
-        "cpu_model": model,
-        "kind": "oracle",
-        "sample": "%d of %d sequences (all %d KV heads, %d tokens, %d queries each): store of the "
-                  "%d new tokens + binary64 verify, %d reps, %.3f s per step" % (
-                      nb, B, Hk, S, N * Hq, N, reps, per_step),
-    }
+
+    def leg(nthreads):
+        _omp_set_threads(nthreads)
+        # sample: the first nb sequences (all of their KV heads), as many as
+        # give every thread a (b, hk) unit -- the oracle's verify, the bulk of
+        # the step, runs one thread per unit; the sequences are stored once
+        # outside the timing
+        nb = min(B, max(1, nthreads // Hk))
+        cache = np.zeros(oracle.cache_bytes(preset, nb, Hk, S), np.uint8)
+        si, po = synth.token_lists(nb, S)
+        oracle.store(preset, cache, nb, Hk, S, synth.rows(inp["K"][:nb]), synth.rows(inp["V"][:nb]), si, po)
+        si_n, po_n = synth.token_lists(nb, S, S - N, S)
+        Kn = synth.rows(inp["K"][:nb], S - N, S)
+        Vn = synth.rows(inp["V"][:nb], S - N, S)
+        Q = np.ascontiguousarray(inp["Q"][:, :nb])
+        sl = inp["seq_lens"][:nb]
+        reps, t_total = 0, 0.0
+        while t_total < seconds or reps == 0:
+            t0 = time.perf_counter()
+            oracle.store(preset, cache, nb, Hk, S, Kn, Vn, si_n, po_n)
+            oracle.verify(preset, cache, nb, Hk, S, Q, sl, Hq, cfg["causal"])
+            t_total += time.perf_counter() - t0
+            reps += 1
+        per_step = t_total / reps
+        kv = nb * S * Hk * slot
+        return {
+            "value": round(kv / per_step / 1e9, 4),
+            "unit": "GB/s",
+            "cores": min(nthreads, nb * Hk),
+            "kind": "oracle",
+            "sample": "%d of %d sequences (all %d KV heads, %d tokens, %d queries each): store of the "
+                      "%d new tokens + binary64 verify, %d reps, %.3f s per step" % (
+                          nb, B, Hk, S, N * Hq, N, reps, per_step),
+        }
+
+    rec = leg(threads)
+    rec["threads_available"] = threads
+    rec["cpu_model"] = model
+    rec["single_thread"] = leg(1)
+    _omp_set_threads(threads)
+    return rec
 
 
 if __name__ == "__main__":

@@ -182,7 +182,10 @@ int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int
  *             n_spec speculative ones included (cached_len = seq_lens[b] - n_spec)
  *   causal    1: query n attends to tokens [0, cached_len + n + 1);
  *             0: every query attends to tokens [0, seq_lens[b])
- *   num_splits  key-range partitions per (b, hk), 0 = auto (at most 256 are used)
+ *   num_splits  key-range partitions per (b, hk), 0 = auto; at most
+ *             min(1024, ceil(ceil(max_seq / 32) / 4)) are used (one range
+ *             covers at least four 32-token tiles); tqkv_verify_num_splits
+ *             returns the count a call will use
  *   sm_scale  softmax scale, 0 = 1/sqrt(128)
  *   out       device, fp32 [n_spec, B, Hq, 128], 16-byte aligned
  *   workspace device, 256-byte aligned, >= tqkv_verify_workspace_bytes(...)

@@ -130,16 +130,20 @@ def test_paged_verify_table_entries_outside_the_pool(preset):
 
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
 @pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
-@pytest.mark.parametrize("N", [8, 16])  # 16 x 4 row tiles: the store runs as its own launch
-def test_store_verify(preset, paged, N):
+# (8, 16): one 64-row work-group per KV head; (16, 16): 16 x 4 row tiles, the
+# store runs as its own launch; (8, 32): 128 rows, two 64-row work-groups per
+# KV head that both quantise the new tokens inside the verify launch
+@pytest.mark.parametrize("N,Hq", [(8, 16), (16, 16), (8, 32)], ids=lambda x: str(x))
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_store_verify(preset, paged, N, Hq, num_splits):
     rng = np.random.default_rng(41)
-    B, Hq, Hk, lens, max_pages, num_pages = 2, 16, 2, (203, 166), 14, 40
+    B, Hk, lens, max_pages, num_pages = 2, 2, (203, 166), 14, 40
     K, V = _kv(rng, B, 203, Hk)
     Q = rng.standard_normal((N, B, Hq, 128)).astype(np.float32)
     sl = np.array(lens, np.int32)
     Kn = np.stack([K[np.arange(B), sl - N + n] for n in range(N)])  # [N, B, Hk, 128]
     Vn = np.stack([V[np.arange(B), sl - N + n] for n in range(N)])
-    print("store_verify", PNAME[preset], "paged" if paged else "contiguous", N, flush=True)
+    print("store_verify", PNAME[preset], "paged" if paged else "contiguous", N, Hq, num_splits, flush=True)
     if paged:
         table, si, po, slots = _layout(lens, max_pages, num_pages, seed=42)
         ref_pool = np.zeros(oracle.paged_cache_bytes(preset, Hk, num_pages), np.uint8)
@@ -160,7 +164,7 @@ def test_store_verify(preset, paged, N):
         old = po < sl[si] - N
         tq.tqkv_store(cache, to_dev(np.ascontiguousarray(K[si[old], po[old]])),
                       to_dev(np.ascontiguousarray(V[si[old], po[old]])), to_dev(si[old]), to_dev(po[old]))
-    out = tq.tqkv_store_verify(cache, to_dev(Kn), to_dev(Vn), to_dev(Q), to_dev(sl), N, Hq, True)
+    out = tq.tqkv_store_verify(cache, to_dev(Kn), to_dev(Vn), to_dev(Q), to_dev(sl), N, Hq, True, num_splits)
     torch.cuda.synchronize()
     got = cache.buffer.cpu().numpy()
     assert np.array_equal(got, ref_pool), "%d bytes differ" % int((got != ref_pool).sum())

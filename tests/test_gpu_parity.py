@@ -7,6 +7,8 @@ rtol 1e-2 (the tolerance of the pages' integration test, Part 6 of
 "Speculative decoding on Intel Arc: TurboQuant KV + a fused N_spec kernel"),
 with NaN exactly where the oracle has NaN.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -27,6 +29,13 @@ def _small(preset, **kw):
     cfg = dict(preset=preset, N=8, B=2, Hq=16, Hk=2, S=203, causal=True, q_dtype=np.float32, seed=7)
     cfg.update(kw)
     return cfg
+
+
+@functools.lru_cache(maxsize=2)
+def _config_inputs(name):
+    """Inputs of a named configuration, kept for the large ones (decode: 4.3 GB,
+    about a minute to draw) so the store and verify tests draw them once."""
+    return synth.make_inputs(synth.config(name))
 
 
 def _oracle_cache(cfg, inp, max_seq=None):
@@ -59,13 +68,20 @@ def test_store_bit_exact_small(preset, seed):
     assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
 
 
-@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc"])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc", "decode_k3v4_nc",
+                                  "long_k3v4_nc"])
 def test_store_bit_exact_config(name):
+    """The whole cache of every configuration, byte for byte (decode: 8.4M
+    token-heads, 1 GB; long context: 1M token-heads)."""
     cfg = synth.config(name)
-    inp = synth.make_inputs(cfg)
-    print("store", name, flush=True)
+    print("store", name, "generating inputs", flush=True)
+    inp = _config_inputs(name) if name in ("decode_k3v4_nc", "long_k3v4_nc") else synth.make_inputs(cfg)
+    print("store", name, "oracle", flush=True)
     ref = _oracle_cache(cfg, inp)
+    print("store", name, "gpu", flush=True)
     got = gpu_store_all(cfg, inp).buffer.cpu().numpy()
+    torch.cuda.empty_cache()
     assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
 
 
@@ -122,6 +138,45 @@ def test_verify_small(preset, causal, q_dtype):
         assert_close(got, ref, what="num_splits=%d" % ns)
 
 
+# Inputs at the edges of the binary16 operand precision: sharper softmax
+# (queries times 2 and 4), outlier key channels (two coordinates 20 times
+# larger, which also set every FP8 token scale), and values far from zero
+# (mean 50: the value zero point, not the spread, dominates each output).
+def _envelope(inp, case):
+    if case == "q_x2":
+        inp["Q"] = (inp["Q"] * 2).astype(inp["Q"].dtype)
+    elif case == "q_x4":
+        inp["Q"] = (inp["Q"] * 4).astype(inp["Q"].dtype)
+    elif case == "key_outliers":
+        K = inp["K"].astype(np.float32)
+        K[..., [3, 77]] *= 20
+        inp["K"] = K.astype(np.float16)
+    elif case == "v_mean_50":
+        inp["V"] = (inp["V"].astype(np.float32) + 50).astype(np.float16)
+    return inp
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("case", ["q_x2", "q_x4", "key_outliers", "v_mean_50"])
+@pytest.mark.parametrize("rows", [64, 32, 8], ids=lambda r: "rows%d" % r)
+def test_verify_precision_envelope(preset, case, rows):
+    """The envelope cases in each row path (64 rows: eight-wavefront
+    work-groups; 32: one row tile; 8: the transposed few-row path), with one
+    key range and with eight, against the oracle's tolerance."""
+    N = {64: 8, 32: 4, 8: 1}[rows]
+    cfg = _small(preset, N=N, S=1000, seed=31)
+    inp = _envelope(synth.make_inputs(cfg), case)
+    inp["seq_lens"] = np.array([1000, 777], np.int32)
+    print("verify envelope", PNAME[preset], case, rows, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"], inp["seq_lens"],
+                        cfg["Hq"], cfg["causal"])
+    cache = gpu_store_all(cfg, inp)
+    for ns in (1, 8):
+        assert tq.tqkv_verify_num_splits(cache, N, cfg["Hq"], ns) == ns
+        assert_close(_gpu_verify(cache, cfg, inp, num_splits=ns), ref, what="%s splits=%d" % (case, ns))
+
+
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
 @pytest.mark.parametrize("scale", [0.02, 0.15, 0.3])
 def test_verify_explicit_scale(preset, scale):
@@ -161,12 +216,16 @@ def test_verify_shapes(preset, shape):
 
 
 @pytest.mark.parametrize("name", ["tiny_k8v4", "poc_k8v4", "poc_k3v4_nc", "poc_k4v4_nc"])
-def test_verify_config_full(name):
+@pytest.mark.parametrize("seed", [None] + list(synth.HELD_OUT_SEEDS))
+def test_verify_config_full(name, seed):
     """Every output of the small configurations against the oracle, in the
-    launch configuration the benchmark times (auto splits)."""
+    launch configuration the benchmark times (auto splits), at the
+    configuration's seed and at the held-out seeds."""
     cfg = synth.config(name)
+    if seed is not None:
+        cfg["seed"] = seed
     inp = synth.make_inputs(cfg)
-    print("verify", name, flush=True)
+    print("verify", name, "seed", cfg["seed"], flush=True)
     ocache = _oracle_cache(cfg, inp)
     ref = oracle.verify(cfg["preset"], ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"],
                         inp["seq_lens"], cfg["Hq"], cfg["causal"])
@@ -183,20 +242,26 @@ def test_verify_config_sampled(name):
     """Large configurations: full GPU run, oracle on sampled (b, hk) units."""
     cfg = synth.config(name)
     print("verify sampled", name, "generating inputs", flush=True)
-    inp = synth.make_inputs(cfg)
+    inp = _config_inputs(name)
     cache = gpu_store_all(cfg, inp)
     got = _gpu_verify(cache, cfg, inp)
     del cache
     torch.cuda.empty_cache()
     G = cfg["Hq"] // cfg["Hk"]
-    rng = np.random.default_rng(5)
-    units = [(0, 0), (cfg["B"] - 1, cfg["Hk"] - 1)] + [
-        (int(rng.integers(cfg["B"])), int(rng.integers(cfg["Hk"]))) for _ in range(2)]
-    for b, hk in units:
-        heads = [hk * G, hk * G + G - 1]
-        print("  oracle unit", b, hk, heads, flush=True)
-        ref = oracle_unit(oracle, cfg, inp, b, hk, heads=heads)
-        assert_close(got[:, b, heads], ref, what="%s b=%d hk=%d" % (name, b, hk))
+    # every (b, hk) unit when there are at most 16 (long context: 4), else
+    # the first, the last and 14 other distinct units; all query heads of each
+    n_units = cfg["B"] * cfg["Hk"]
+    if n_units <= 16:
+        picks = list(range(n_units))
+    else:
+        rng = np.random.default_rng(5)
+        picks = [0, n_units - 1] + [int(u) for u in rng.choice(np.arange(1, n_units - 1), 14, replace=False)]
+    assert len(set(picks)) == min(16, n_units)
+    for u in picks:
+        b, hk = divmod(u, cfg["Hk"])
+        print("  oracle unit", b, hk, flush=True)
+        ref = oracle_unit(oracle, cfg, inp, b, hk)
+        assert_close(got[:, b, hk * G:(hk + 1) * G], ref, what="%s b=%d hk=%d" % (name, b, hk))
 
 
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)

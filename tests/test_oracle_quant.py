@@ -130,6 +130,31 @@ def test_k8_relative_error_and_scale():
         assert np.max(np.abs(dec)) <= 448
 
 
+def test_k8_codes_are_torch_e4m3fn_of_x_over_rounded_scale():
+    """Each k8 key code is the OCP E4M3 ("e4m3fn") encoding, round to nearest
+    even, of x / s_h evaluated in binary32, where s_h is the binary16 scale
+    (Part 6 of the speculative-decoding page keeps FP8 keys with one scale
+    per token).  torch's float8_e4m3fn conversion is the independent
+    reference; every |x / s_h| stays below 464, where it needs no
+    saturation.  The rounding of the scale to binary16 matters: with the
+    unrounded binary32 scale some codes come out different."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(81)
+    flips = 0
+    for _ in range(300):
+        k = (rng.standard_normal(128) * rng.uniform(0.01, 50)).astype(np.float16)
+        codes, sh = oracle.quant_key_k8(k)
+        s = np.float32(h2f(sh))
+        x = k.astype(np.float32) / s
+        assert np.all(np.abs(x) < 464)
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref), np.flatnonzero(codes != ref)[:5]
+        s32 = np.float32(np.max(np.abs(k.astype(np.float32)))) / np.float32(448)
+        alt = torch.from_numpy(k.astype(np.float32) / s32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        flips += int(not np.array_equal(alt, codes))
+    assert flips > 0
+
+
 def test_k8_zero_vector():
     codes, sh = oracle.quant_key_k8(np.zeros(128, np.float16))
     assert sh == 0 and np.all(codes == 0)
