@@ -122,14 +122,21 @@ typedef struct tqkv_paged_cache {
                                    16 * max_pages per sequence, <= TQKV_MAX_PAGES_PER_SEQ */
 } tqkv_paged_cache;
 
-/* Bytes per token and KV head: 120 (k3v4_nc), 136 (k4v4_nc) or 198 (k8v4);
- * 0 for a bad preset. */
+/* Bytes per token and KV head ("slot"): 120 (k3v4_nc), 136 (k4v4_nc) or
+ * 198 (k8v4); 0 for a bad preset.  The pages size the cache per token and
+ * KV head ("Speculative decoding on Intel Arc", Part 2, Roofline: a k8v4
+ * slot of 196 B); k8v4 here also keeps the per-token fp16 key scale (+2 B),
+ * and the 3-bit preset packs 128 codes into 48 B next to the same 4-bit
+ * values (Context: 3-4 bits per coordinate). */
 size_t tqkv_slot_bytes(int preset);
 
-/* Bytes per 16-token block: 16 * tqkv_slot_bytes(preset). */
+/* Bytes per 16-token block: 16 * tqkv_slot_bytes(preset) (the 16-token
+ * block is the unit of the pages' paged cache, Part 2, Roofline). */
 size_t tqkv_block_bytes(int preset);
 
-/* Bytes of a whole cache; 0 for invalid arguments. */
+/* Bytes of a whole contiguous cache, B * Hk * ceil(max_seq / 16) blocks (the
+ * Roofline count of Part 2: blocks x 16 tokens x Hk x slot); 0 for invalid
+ * arguments. */
 size_t tqkv_cache_bytes(int preset, int B, int Hk, int D, int max_seq);
 
 /* Bytes of a paged pool of num_pages pages: num_pages * Hk * tqkv_block_bytes(preset);
@@ -165,12 +172,19 @@ int tqkv_paged_store(const tqkv_paged_cache *cache, const void *K, const void *V
                      int T, void *stream);
 
 /* Number of key-range partitions tqkv_verify uses for num_splits (0 = auto)
- * on this cache and shape; 0 for invalid arguments. */
+ * on this cache and shape; 0 for invalid arguments.  The partitions are the
+ * first stage of the pages' two-stage split-KV decode ("Speculative
+ * decoding on Intel Arc", Part 2: NUM_KV_SPLITS ranges per (b, hk), merged
+ * by log-sum-exp in stage 2). */
 int tqkv_verify_num_splits(const tqkv_cache *cache, int n_spec, int Hq, int num_splits);
 
 /* Device workspace tqkv_verify needs, returned through *bytes: when more
  * than one key range is used, the partial softmax states of every range
- * (0 bytes otherwise).  Returns TQKV_OK or a negative tqkv_status. */
+ * (the stage-1 outputs of Part 2's split-KV decode: per row and range a
+ * running max, a sum and a binary16 partial output; 0 bytes otherwise).
+ * The size comes back through a pointer so that the return value can
+ * report an invalid shape or a missing device as a status.
+ * Returns TQKV_OK or a negative tqkv_status. */
 int tqkv_verify_workspace_bytes(const tqkv_cache *cache, int n_spec, int Hq, int num_splits,
                                 size_t *bytes);
 
