@@ -49,6 +49,7 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -1717,6 +1718,21 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
         for (int dt = 0; dt < 4; ++dt)
             acc[dt][qt] = floatx16{0};
     }
+    // Lloyd-Max keys: the subtrahend enters the score MFMA chain as a
+    // 32x32x8 product of a ones column pair (k = 0, 1 in lanes 0-31) with the
+    // row's -msub split into binary16 hi + lo (exact to 2^-22 relative),
+    // instead of 32 subtractions per tile
+    const half4_t sub_ones = (h == 0) ? half4_t{(_Float16)1.0f, (_Float16)1.0f, (_Float16)0.0f, (_Float16)0.0f}
+                                      : half4_t{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+    uint32_t sub_hl[NQT]; // lanes 0-31: binary16 (-hi, -lo) of the row's subtrahend
+    auto split_sub = [&](float x) -> uint32_t {
+        const _Float16 hi = (_Float16)x;
+        const _Float16 lo = (_Float16)(x - (float)hi);
+        return (h == 0) ? __builtin_bit_cast(uint32_t, half2_t{-hi, -lo}) : 0u;
+    };
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+        sub_hl[qt] = 0u;
     // tile i: S = K Q^T, the lazy online-softmax rescale (the running max
     // moves only when a score exceeds it by more than kRescaleSlack; an
     // unset max takes the tile's maximum), P = exp2(S - m) in binary16, the
@@ -1740,6 +1756,13 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                 f[s2].h = *reinterpret_cast<const half8_t *>(slot + s2 * L_::kBlockBytes + L_::kMeta0 + 16 * h);
         }
         floatx16 S[NQT];
+        if constexpr (kLloydMax<PRESET>) {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const half4_t bsub = __builtin_bit_cast(half4_t, make_uint2(sub_hl[qt], 0u));
+                S[qt] = __builtin_amdgcn_mfma_f32_32x32x8f16(sub_ones, bsub, floatx16{0}, 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             half8_t A;
@@ -1749,20 +1772,19 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                 A = key_operand_fp8(kr, ks);
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt)
-                S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qop(qt, ks), ks == 0 ? floatx16{0} : S[qt], 0, 0, 0);
+                S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    A, qop(qt, ks), (ks == 0 && !kLloydMax<PRESET>) ? floatx16{0} : S[qt], 0, 0, 0);
         }
-        // scores relative to the subtrahend (FP8: each column times its
-        // token's key scale); register v holds token tok0 + 8h + 16 (v / 8)
-        // + v % 8
+        // FP8: each score column times its token's key scale, relative to
+        // the subtrahend (Lloyd-Max: already in the MFMA chain); register v
+        // holds token tok0 + 8h + 16 (v / 8) + v % 8
+        if constexpr (!kLloydMax<PRESET>) {
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
+            for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                if constexpr (kLloydMax<PRESET>)
-                    S[qt][v] -= msub[qt];
-                else
+                for (int v = 0; v < 16; ++v)
                     S[qt][v] = __builtin_fmaf(S[qt][v], (float)f[v >> 3].h[v & 7], -msub[qt]);
-            }
+        }
         if constexpr (MASKED) {
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -1798,6 +1820,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                 zs[qt] *= alpha;
                 m[qt] = mnew;
                 msub[qt] = snew;
+                sub_hl[qt] = split_sub(snew);
                 thr[qt] = (mnew == -__builtin_inff()) ? -__builtin_inff() : kRescaleSlack;
             }
         }
