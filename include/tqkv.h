@@ -156,7 +156,8 @@ size_t tqkv_paged_cache_bytes(int preset, int Hk, int D, int num_pages);
  * code = clamp(rint((v - zero) / scale), 0, 15).  The bytes written are
  * bit-identical to the specification (all arithmetic IEEE binary32, RNE).
  * (seq_idx, pos) pairs must be distinct within one call; an entry out of
- * range is skipped (nothing written).  T == 0 is a no-op.
+ * range is skipped (nothing written).  T == 0 is a no-op; T rounded up to a
+ * multiple of 16, times Hk, must not exceed 2^31 - 1 (TQKV_ERR_UNSUPPORTED).
  * Returns TQKV_OK or a negative tqkv_status. */
 int tqkv_store(const tqkv_cache *cache, const void *K, const void *V, const int32_t *seq_idx,
                const int32_t *pos, int T, void *stream);

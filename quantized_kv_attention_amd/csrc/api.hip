@@ -350,7 +350,8 @@ int store_impl(int preset, int Hk, void *base, const tqkv_cache *c, const tqkv_p
         return TQKV_ERR_ARG;
     if (!aligned(K, 2) || !aligned(V, 2) || !aligned(seq_idx, 4) || !aligned(pos, 4) || !aligned(slot_mapping, 4))
         return TQKV_ERR_ALIGN;
-    if ((long)T * Hk > (long)INT32_MAX * 4)
+    // the store kernel indexes (16-token chunk, head) pairs in 32 bits
+    if ((long)((T + 15) / 16) * 16 * Hk > (long)INT32_MAX)
         return TQKV_ERR_UNSUPPORTED;
     int cus = current_device_cus();
     if (cus < 0)

@@ -61,21 +61,18 @@ __device__ inline float group_tree_sumsq(const float (&x)[kPer], int lane)
 __device__ inline void group_wht(float (&x)[kPer], int lane)
 {
     const int j = lane & 7;
+    // lane pairs: own + partner, or partner - own, as fma(+-1, own, partner)
+    // (one rounding of an exact sum: the same value as the add or subtract)
+    const float s1 = (j & 1) ? -1.0f : 1.0f, s2 = (j & 2) ? -1.0f : 1.0f, s4 = (j & 4) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-        const float p = gxor<1>(x[m], lane);
-        x[m] = (j & 1) ? __fsub_rn(p, x[m]) : __fadd_rn(x[m], p);
-    }
+    for (int m = 0; m < kPer; ++m)
+        x[m] = __builtin_fmaf(s1, x[m], gxor<1>(x[m], lane));
 #pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-        const float p = gxor<2>(x[m], lane);
-        x[m] = (j & 2) ? __fsub_rn(p, x[m]) : __fadd_rn(x[m], p);
-    }
+    for (int m = 0; m < kPer; ++m)
+        x[m] = __builtin_fmaf(s2, x[m], gxor<2>(x[m], lane));
 #pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-        const float p = gxor<4>(x[m], lane);
-        x[m] = (j & 4) ? __fsub_rn(p, x[m]) : __fadd_rn(x[m], p);
-    }
+    for (int m = 0; m < kPer; ++m)
+        x[m] = __builtin_fmaf(s4, x[m], gxor<4>(x[m], lane));
 #pragma unroll
     for (int hb = 1; hb < kPer; hb <<= 1)
 #pragma unroll
@@ -87,22 +84,18 @@ __device__ inline void group_wht(float (&x)[kPer], int lane)
             }
 }
 
-// rint(a / s) clamped to [0, 15] with a / s the correctly rounded binary32
-// quotient (s > 0).  The quotient a * (1 / s) of the two roundings differs
-// from it by under 3e-6 for |a / s| <= 16; when no integer + 1/2 lies within
-// 4e-6 of it both round to the same integer, otherwise (rarely) the exact
-// division decides.  Outside [-0.5, 15.5] the clamp decides alone.
-__device__ inline uint32_t value_code(float a, float s, float rs)
+// Value codes clamp(rint(a / s), 0, 15) with a / s the correctly rounded
+// binary32 quotient (s > 0).  The product a * (1 / s) of two roundings
+// differs from that quotient by under 3e-6 for |a / s| <= 16, so where no
+// integer + 1/2 lies within 4e-6 of it both round to the same integer;
+// near such a point (rarely) the exact division decides, for the whole
+// wavefront at once.  Outside [-0.5, 15.5] the clamp decides alone.
+__device__ inline bool code_near_tie(float q)
 {
-    const float q = __fmul_rn(a, rs);
     const float f = q - floorf(q);
-    float r;
-    if (__builtin_expect(q > -1.0f && q < 16.0f && fabsf(f - 0.5f) < 4e-6f, 0))
-        r = rintf(__fdiv_rn(a, s));
-    else
-        r = rintf(q);
-    return (r > 0.0f) ? ((r >= 15.0f) ? 15u : (uint32_t)r) : 0u; // NaN -> 0
+    return q > -1.0f && q < 16.0f && fabsf(f - 0.5f) < 4e-6f;
 }
+__device__ inline uint32_t code_clamp(float r) { return (r > 0.0f) ? ((r >= 15.0f) ? 15u : (uint32_t)r) : 0u; } // NaN -> 0
 
 template <int PRESET>
 __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
@@ -113,10 +106,12 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
     // consecutive tokens of one head (normally one cache block) are
     // quantised by two neighbouring wavefronts, so each block's lines are
     // written in full at about the same time
-    const long gi = (long)blockIdx.x * (kStoreThreads / kGroup) + (threadIdx.x >> 3);
-    const long rest = gi >> 4;
-    const int hk = (int)(rest % a.Hk);
-    const long t_raw = (rest / a.Hk) * 16 + (gi & 15);
+    // (32-bit index arithmetic: at most 2^31 / 4 * 16 / 16 chunk-heads, the
+    // limit the host checks on T * Hk)
+    const uint32_t gi = blockIdx.x * (kStoreThreads / kGroup) + (threadIdx.x >> 3);
+    const uint32_t rest = gi >> 4;
+    const int hk = (int)(rest % (uint32_t)a.Hk);
+    const long t_raw = (long)(rest / (uint32_t)a.Hk) * 16 + (gi & 15);
     const bool live = t_raw < a.T;
     const int t = live ? (int)t_raw : 0; // groups past the last token compute on token 0, store nothing
     const long th = (long)t * a.Hk + hk;
@@ -305,14 +300,27 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
     const uint16_t sch = quant::f2h(__fdiv_rn(__fsub_rn(mx, mn), 15.0f));
     const float sc = quant::h2f_q(sch);
     const float rs = __fdiv_rn(1.0f, sc);
+    float qv[kPer];
+    bool near = false;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+        qv[m] = __fmul_rn(__fsub_rn(v[m], zero), rs);
+        near |= code_near_tie(qv[m]);
+    }
+    if (__builtin_expect(__any(near), 0)) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            if (code_near_tie(qv[m]))
+                qv[m] = __fdiv_rn(__fsub_rn(v[m], zero), sc);
+    }
     if (blk) {
         uint8_t *vb = blk + L::kValOff;
 #pragma unroll
         for (int i = 0; i < kPer / 2; ++i) {
             uint32_t c0 = 0u, c1 = 0u;
             if (sc != 0.0f) {
-                c0 = value_code(__fsub_rn(v[2 * i], zero), sc, rs);
-                c1 = value_code(__fsub_rn(v[2 * i + 1], zero), sc, rs);
+                c0 = code_clamp(rintf(qv[2 * i]));
+                c1 = code_clamp(rintf(qv[2 * i + 1]));
             }
             vb[val_byte_offset(tb, 8 * j + i)] = (uint8_t)(c0 | (c1 << 4));
         }
