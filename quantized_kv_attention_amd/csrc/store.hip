@@ -229,11 +229,13 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
                 w[i] |= gxor<1>(w[i], lane);
             }
             if (blk && j < 3) {
-                uint4 *kd = reinterpret_cast<uint4 *>(blk + tb * L::kKeyBytesPerToken);
-                const uint4 o0 = make_uint4(w[0], w[1], w[2], w[3]);
-                const uint4 o1 = make_uint4(w[4], w[5], w[6], w[7]);
-                const uint4 o2 = make_uint4(w[8], w[9], w[10], w[11]);
-                kd[j] = (j == 0) ? o0 : ((j == 1) ? o1 : o2);
+                // lane j writes words 4j .. 4j + 3 (per-word selects: a
+                // select of whole vectors went through a stack copy)
+                uint32_t o[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    o[q4] = ((j == 0) ? w[q4] : 0u) | ((j == 1) ? w[4 + q4] : 0u) | ((j == 2) ? w[8 + q4] : 0u);
+                reinterpret_cast<uint4 *>(blk + tb * L::kKeyBytesPerToken)[j] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         } else {
             // coordinate 8m + e -> key dword m, byte e % 4, nibble e / 4
@@ -248,13 +250,12 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
                 w[m] |= gxor<1>(w[m], lane);
             }
             if (blk && j < 4) {
-                uint4 *kd = reinterpret_cast<uint4 *>(blk + tb * L::kKeyBytesPerToken);
-                uint4 o = make_uint4(w[0], w[1], w[2], w[3]);
+                uint32_t o[4];
 #pragma unroll
-                for (int q4 = 1; q4 < 4; ++q4)
-                    if (j == q4)
-                        o = make_uint4(w[4 * q4], w[4 * q4 + 1], w[4 * q4 + 2], w[4 * q4 + 3]);
-                kd[j] = o;
+                for (int q4 = 0; q4 < 4; ++q4)
+                    o[q4] = ((j == 0) ? w[q4] : 0u) | ((j == 1) ? w[4 + q4] : 0u) | ((j == 2) ? w[8 + q4] : 0u) |
+                            ((j == 3) ? w[12 + q4] : 0u);
+                reinterpret_cast<uint4 *>(blk + tb * L::kKeyBytesPerToken)[j] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
     } else {
