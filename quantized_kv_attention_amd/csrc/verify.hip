@@ -52,6 +52,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 32;        // tokens per inner-loop step
 constexpr int kWaves = 4;        // wavefronts per work-group
@@ -1982,7 +1983,6 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     gather(0);
 
     // ------------------------------------------- output or partial state
-    constexpr int kOStride = kD + 4;
     auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
     if (a.nsplit > 1 && aa == 0 && h == 0 && tile0 + mq < a.nrt) {
         float *pm = reinterpret_cast<float *>(&a.part_ml[part_slot(tile0 + mq) + lrow]);
@@ -1996,47 +1996,39 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             for (int k = 0; k < 4; ++k)
                 O[j][k] = __builtin_nanf("");
     }
-    __syncthreads(); // every wavefront has read the merge buffer
-    float *ob = reinterpret_cast<float *>(lds); // [RP rows][kOStride]
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4 *>(ob + (32 * mq + lrow) * kOStride + 4 * (8 * aa + 4 * h + j)) =
-            make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
-    __syncthreads();
+    // Outputs straight from the registers (no LDS staging): this thread's
+    // row 32 mq + lrow, coordinates 4 (8 aa + 4h + j) + 0..3 for j = 0..3,
+    // as four binary32 (the output) or four binary16 (a partial state).
+    // (A staging round through LDS for whole-row stores cost 0.2-0.6 us
+    // per PoC call more.)
+    if (tile0 + mq >= a.nrt)
+        return;
     if (a.nsplit == 1) {
+        const int grow = row0 + 32 * mq + lrow;
+        if (grow >= Rb)
+            return;
+        const int n = row_token(grow), g = grow - n * a.G;
+        float *dst = a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD;
 #pragma unroll
-        for (int k = 0; k < RP * kD / 4 / 512; ++k) {
-            const int f4 = threadIdx.x + 512 * k;
-            const int r = f4 >> 5, c = (f4 & 31) * 4;
-            const int grow = row0 + r;
-            if (grow >= Rb)
-                continue;
-            const int n = row_token(grow), g = grow - n * a.G;
-            float *dst = a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD;
-            *reinterpret_cast<float4 *>(dst + c) = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(dst + 4 * (8 * aa + 4 * h + j)) = make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
+        return;
+    }
+    _Float16 *po = a.part_o + (part_slot(tile0 + mq) + lrow) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            // binary16 range, NaN kept
+            const float x0 = O[j][2 * q], x1 = O[j][2 * q + 1];
+            float p = fminf(fmaxf(x0, -65504.0f), 65504.0f);
+            float r2 = fminf(fmaxf(x1, -65504.0f), 65504.0f);
+            p = (x0 == x0) ? p : x0;
+            r2 = (x1 == x1) ? r2 : x1;
+            w2[q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
         }
-    } else {
-#pragma unroll
-        for (int k = 0; k < RP * kD / 8 / 512; ++k) {
-            const int e8 = threadIdx.x + 512 * k;
-            const int r = e8 >> 4, c = (e8 & 15) * 8;
-            if (tile0 + (r >> 5) >= a.nrt)
-                continue;
-            _Float16 *pbase_o = a.part_o + (part_slot(tile0 + (r >> 5)) + (r & 31)) * kD;
-            const float4 x0 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c);
-            const float4 x1 = *reinterpret_cast<const float4 *>(ob + r * kOStride + c + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint32_t w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float p = fminf(fmaxf(xs[2 * q], -65504.0f), 65504.0f);
-                float r2 = fminf(fmaxf(xs[2 * q + 1], -65504.0f), 65504.0f);
-                p = (xs[2 * q] == xs[2 * q]) ? p : xs[2 * q];
-                r2 = (xs[2 * q + 1] == xs[2 * q + 1]) ? r2 : xs[2 * q + 1];
-                w[q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
-            }
-            __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(pbase_o + c));
-        }
+        __builtin_nontemporal_store(u32x2{w2[0], w2[1]}, reinterpret_cast<u32x2 *>(po + 4 * (8 * aa + 4 * h + j)));
     }
 }
 
