@@ -1501,6 +1501,19 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
 
     // ------------------------------------------------------------ prologue
+    // 0. fused store: this wavefront's first new token-head(s) are loaded
+    //    now, so their memory latency overlaps the query and ring loads
+    const int tn0 = (a.Knew != nullptr) ? L - nq : L;
+    const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile);
+    quant::TokenHead nx1{0, 0, 0, 0}, nx2{0, 0, 0, 0};
+    if (wn0 + wave < wn1) {
+        const int t = wn0 + wave, t2 = min(t + kW, wn1 - 1);
+        const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+        const size_t src2 = ((size_t)(qt0 + (t2 - tn0) * qts) * a.Hk + hk) * kD;
+        nx1 = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+        nx2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+    }
+
     // 1. raw query rows -> LDS, queued before any ring load
     {
         const int esz = a.q_f16 ? 2 : 4;
@@ -1555,8 +1568,6 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             return (p >= 0 && p < a.npages) ? a.wbase + ((size_t)p * a.Hk + hk) * L_::kBlockBytes : nullptr;
         }
     };
-    const int tn0 = (a.Knew != nullptr) ? L - nq : L;
-    const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile);
     // Ring prefill: one tile per wavefront now (if it holds no new token),
     // the rest once the query rows are prepared.  Loads issued here compete
     // with the query loads for the memory system, and a wavefront whose
@@ -1574,10 +1585,13 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     if (wn0 < wn1) {
         for (int t = wn0 + wave; t < wn1; t += 2 * kW) {
             const int t2 = t + kW;
-            const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
-            const size_t src2 = ((size_t)(qt0 + (min(t2, wn1 - 1) - tn0) * qts) * a.Hk + hk) * kD;
-            const quant::TokenHead x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
-            const quant::TokenHead x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+            quant::TokenHead x = nx1, x2 = nx2;
+            if (t != wn0 + wave) {
+                const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+                const size_t src2 = ((size_t)(qt0 + (min(t2, wn1 - 1) - tn0) * qts) * a.Hk + hk) * kD;
+                x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+                x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+            }
             uint8_t *blk = store_block(t);
             if (t2 < wn1) {
                 const quant::Record r1 = quant::quantize_record<PRESET>(x, lane);
