@@ -108,6 +108,44 @@ def test_store_edge_vectors(preset):
     assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
 
 
+def _binary16_up_to(a):
+    """Every finite binary16 x with |x| <= a, both signs (+0 and -0 included)."""
+    mags = np.arange(0x7C00, dtype=np.uint16).view(np.float16)
+    mags = mags[mags <= np.float16(a)]
+    return np.concatenate([mags, -mags])
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_store_every_binary16_value(preset):
+    """Every finite binary16 below each of a range of maxima (subnormal, tiny,
+    near 1, 448, the binary16 maximum): each token-head holds its maximum and
+    127 values at most as large, so the FP8 key codes meet every quotient
+    x / s that their scale s allows, and the value codes every (v - zero) / s
+    of a wide range (rounding boundaries and ties included)."""
+    maxima = [2.0**-24, 2.0**-17, 2.0**-14, 1e-3, 0.1, 1.0, 1.5, np.pi, 100.0, 448.0, 1000.0, 3e4, 65504.0]
+    rng = np.random.default_rng(5)
+    rows = []
+    for a in maxima:
+        xs = rng.permutation(_binary16_up_to(a))
+        for i in range(0, len(xs), 127):
+            chunk = xs[i:i + 127]
+            if len(chunk) < 127:
+                chunk = np.concatenate([chunk, rng.choice(xs, 127 - len(chunk))])
+            rows.append(np.concatenate([[np.float16(a)], chunk]))
+    K = np.stack(rows).astype(np.float16)[:, None, :]
+    V = np.ascontiguousarray(K[:, :, ::-1])
+    T = len(rows)
+    si = np.zeros(T, np.int32)
+    po = np.arange(T, dtype=np.int32)
+    print("store every binary16", PNAME[preset], T, "token-heads", flush=True)
+    ref = np.zeros(oracle.cache_bytes(preset, 1, 1, T), np.uint8)
+    oracle.store(preset, ref, 1, 1, T, K, V, si, po)
+    cache = tq.Cache(preset, 1, 1, T)
+    tq.tqkv_store(cache, to_dev(K), to_dev(V), to_dev(si), to_dev(po))
+    got = cache.buffer.cpu().numpy()
+    assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
+
+
 def test_store_skips_out_of_range_and_empty():
     cache = tq.Cache(synth.K8V4, 2, 1, 20)
     K = torch.ones((3, 1, 128), dtype=torch.float16, device="cuda")
