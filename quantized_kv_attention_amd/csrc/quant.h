@@ -39,39 +39,62 @@ __device__ inline uint16_t f2h(float f)
     return __half_as_ushort(__float2half_rn(f));
 }
 
-__device__ inline float centroid(int c)
+// Lloyd-Max cells by binary search over the sorted thresholds: the cell is
+// #{j : y >= tau_j} either way (a NaN compares false at every step and lands
+// in cell 0), in three comparisons for 8 levels and four for 16 instead of
+// seven and fifteen.  Thresholds and levels come from lane tables through
+// ds_bpermute (lane l holds tau_(l % 16), and level l % 8 or, for 16 levels,
+// the magnitude |c16_(8 + l % 8)|); the probe moves by integer steps, so
+// there is no select of floating-point constants (the compiler turned
+// nested ones into branches) and no register per constant.
+template <int NL> __device__ inline uint32_t threshold_lane_table(int lane)
 {
-    // select chain over the 8 constant levels (keeps the table in immediates)
-    float lo = (c & 2) ? ((c & 1) ? kCentroid[3] : kCentroid[2]) : ((c & 1) ? kCentroid[1] : kCentroid[0]);
-    float hi = (c & 2) ? ((c & 1) ? kCentroid[7] : kCentroid[6]) : ((c & 1) ? kCentroid[5] : kCentroid[4]);
-    return (c & 4) ? hi : lo;
-}
-
-__device__ inline int lloyd_code(float y)
-{
-    int c = 0;
+    const int k = lane & 15;
+    float v = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 7; ++j)
-        c += (y >= kThreshold[j]) ? 1 : 0; // NaN compares false: code 0
-    return c;
+    for (int j = 0; j < NL - 1; ++j)
+        if (k == j)
+            v = (NL == 8) ? kThreshold[j] : kThreshold16[j];
+    return __float_as_uint(v);
 }
-
-// 16 levels: |c16_c| through the symmetry c16_(15-j) = -c16_j (the sign
-// does not enter the norm correction), and the code from 15 thresholds
-__device__ inline float centroid16_abs(int c)
+template <int NL> __device__ inline uint32_t level_lane_table(int lane)
 {
-    const int m = (c >= 8) ? c - 8 : 7 - c; // rank of |c16_c| from zero
-    float lo = (m & 2) ? ((m & 1) ? kCentroid16[11] : kCentroid16[10]) : ((m & 1) ? kCentroid16[9] : kCentroid16[8]);
-    float hi = (m & 2) ? ((m & 1) ? kCentroid16[15] : kCentroid16[14]) : ((m & 1) ? kCentroid16[13] : kCentroid16[12]);
-    return (m & 4) ? hi : lo;
-}
-
-__device__ inline int lloyd_code16(float y)
-{
-    int c = 0;
+    const int k = lane & 7;
+    float v = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 15; ++j)
-        c += (y >= kThreshold16[j]) ? 1 : 0; // NaN compares false: code 0
+    for (int j = 0; j < 8; ++j)
+        if (k == j)
+            v = (NL == 8) ? kCentroid[j] : kCentroid16[8 + j];
+    return __float_as_uint(v);
+}
+// entry byte_idx / 4 of a lane table
+__device__ inline float lane_table_at(uint32_t tab, int byte_idx)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(byte_idx, (int)tab));
+}
+__device__ inline int lloyd_cell8(float y, uint32_t ttab)
+{
+    const bool b2 = y >= kThreshold[3];
+    int i = b2 ? 4 * 5 : 4 * 1; // tau_(4 b2 + 1)
+    const bool b1 = y >= lane_table_at(ttab, i);
+    i += b1 ? 4 : -4; // tau_(2k), k = 2 b2 + b1: the cell pair {2k, 2k + 1}
+    const bool b0 = y >= lane_table_at(ttab, i);
+    return (i >> 2) + (b0 ? 1 : 0);
+}
+// m: the rank of |c16_c| from zero (c - 8 for c >= 8, 7 - c below: the
+// three low bits of c, inverted when bit 3 is clear, since the codebook is
+// symmetric)
+__device__ inline int lloyd_cell16(float y, uint32_t ttab, int &m)
+{
+    const bool b3 = y >= kThreshold16[7];
+    int i = b3 ? 4 * 11 : 4 * 3; // tau_(8 b3 + 3)
+    const bool b2 = y >= lane_table_at(ttab, i);
+    i += b2 ? 8 : -8; // tau_(8 b3 + 4 b2 + 1)
+    const bool b1 = y >= lane_table_at(ttab, i);
+    i += b1 ? 4 : -4; // tau_(2k), k = 4 b3 + 2 b2 + b1: the cell pair {2k, 2k + 1}
+    const bool b0 = y >= lane_table_at(ttab, i);
+    const int c = (i >> 2) + (b0 ? 1 : 0);
+    m = (c & 7) ^ (b3 ? 0 : 7);
     return c;
 }
 
@@ -129,40 +152,53 @@ __device__ inline float wave_tree_sum(float a, int lane)
     return a;
 }
 
-// OCP E4M3 encoding with round-to-nearest-even on the binary32 bit pattern
-// and saturation to +-448; NaN -> 0x7F.
-__device__ inline uint32_t e4m3_rne_sat(float x)
+// OCP E4M3 code of binary32 q (round to nearest even, saturation to +-448,
+// NaN -> 0x7F; the encoding of the FP8 keys), without branches: in the
+// normal range the bit pattern is rounded at bit 20 (ties to even) and the
+// exponent rebiased by 127 - 7; below 2^-6 the code is rint(|q| * 2^9).
+__device__ inline uint32_t e4m3_code(float q)
 {
-    uint32_t u = __float_as_uint(x);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u)
-        return 0x7Fu;
-    float af = __uint_as_float(a);
-    if (af >= 448.0f)
-        return sign | 0x7Eu;
-    if (a < 0x3C800000u) { // below 2^-6: multiples of 2^-9
-        float q = rintf(__fmul_rn(af, 512.0f));
-        return sign | (uint32_t)q;
-    }
-    int e = (int)(a >> 23) - 127 + 7;      // biased e4m3 exponent, 1..15
-    uint32_t keep = (a >> 20) & 7u;        // top three mantissa bits
-    uint32_t rest = a & 0xFFFFFu;          // the 20 bits rounded away
-    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u)))
-        keep += 1;
-    if (keep == 8u) {
-        keep = 0;
-        e += 1;
-    }
-    uint32_t code = ((uint32_t)e << 3) | keep;
-    return sign | (code > 0x7Eu ? 0x7Eu : code);
+    const uint32_t u = __float_as_uint(q), a = u & 0x7FFFFFFFu;
+    const uint32_t rn = (a + 0x7FFFFu + ((a >> 20) & 1u) - (120u << 23)) >> 20;
+    const uint32_t cn = rn < 0x7Eu ? rn : 0x7Eu;
+    const uint32_t cs = (uint32_t)rintf(__fmul_rn(__uint_as_float(a), 512.0f));
+    const uint32_t c = (a < 0x3C800000u) ? cs : cn;
+    return (a > 0x7F800000u) ? 0x7Fu : (((u >> 24) & 0x80u) | c);
 }
 
+// q = x * (1 / s) (two roundings) is within 2^-23 |x / s| of the correctly
+// rounded quotient, i.e. two units in its last place: its E4M3 code can
+// differ from the quotient's only where q lies that close to a rounding
+// boundary: the 20 discarded bits near 0x80000 (normal range), |q| * 2^9
+// near a half-integer (below 2^-6; a 2^-20 error there).  The margins are
+// 4 units and 2^-16.
+__device__ inline bool e4m3_near_boundary(float q)
+{
+    const uint32_t a = __float_as_uint(q) & 0x7FFFFFFFu;
+    const float t = __fmul_rn(__uint_as_float(a), 512.0f);
+    const bool sub = fabsf(t - rintf(t)) > 0.5f - 0x1p-16f;
+    const bool nrm = ((a & 0xFFFFFu) - 0x7FFFCu) < 9u;
+    return (a < 0x3C800000u) ? sub : nrm;
+}
+
+// Value codes clamp(rint(a / s), 0, 15) with a / s the correctly rounded
+// binary32 quotient (s > 0).  The product a * (1 / s) of two roundings
+// differs from that quotient by under 3e-6 for |a / s| <= 16, so where no
+// integer + 1/2 lies within 4e-6 of it both round to the same integer;
+// near such a point (rarely) the exact division decides, for the whole
+// wavefront at once.  The test reuses the rounding: q is within 4e-6 of a
+// half-integer exactly when |q - rint(q)| (an exact difference) exceeds
+// 1/2 - 4e-6.  Outside [-0.5, 15.5] the clamp decides either way.
+__device__ inline bool code_near_tie(float q, float r) { return fabsf(q - r) > 0.5f - 4e-6f; }
+// clamp to [0, 15] of an integral value; NaN -> 0 (fmaxf returns the number)
+__device__ inline uint32_t code_clamp(float r) { return (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f); }
 
 // One token-head's inputs as this lane holds them: coordinates lane and
 // lane + 64 of the key and of the value (fp16 bit patterns).
+// (Held as 32-bit words: four 16-bit fields were packed into two registers
+// right after the loads, which made the wavefront wait for them there.)
 struct TokenHead {
-    uint16_t k0, k1, v0, v1;
+    uint32_t k0, k1, v0, v1;
 };
 
 __device__ inline TokenHead load_token_head(const uint16_t *kp, const uint16_t *vp, int lane)
@@ -192,7 +228,7 @@ __device__ inline Record quantize_record(const TokenHead &in, int lane)
 {
     Record r;
     // ---------------------------------------------------------------- keys
-    float x0 = h2f_q(in.k0), x1 = h2f_q(in.k1);
+    float x0 = h2f_q((uint16_t)in.k0), x1 = h2f_q((uint16_t)in.k1);
     if constexpr (kLloydMax<PRESET>) {
         const float n = sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(x0, x0), __fmul_rn(x1, x1)), lane));
 #pragma unroll
@@ -213,18 +249,21 @@ __device__ inline Record quantize_record(const TokenHead &in, int lane)
         }
         const float rr = __fdiv_rn(1.0f, __fmul_rn(sqrt_rn(128.0f), n));
         const float y0 = __fmul_rn(x0, rr), y1 = __fmul_rn(x1, rr);
+        constexpr int NL = (PRESET == kPresetK3V4) ? 8 : 16;
+        const uint32_t ttab = threshold_lane_table<NL>(lane), ltab = level_lane_table<NL>(lane);
         int c0, c1;
         float q0, q1;
         if constexpr (PRESET == kPresetK3V4) {
-            c0 = lloyd_code(y0);
-            c1 = lloyd_code(y1);
-            q0 = centroid(c0);
-            q1 = centroid(c1);
+            c0 = lloyd_cell8(y0, ttab);
+            c1 = lloyd_cell8(y1, ttab);
+            q0 = lane_table_at(ltab, 4 * c0);
+            q1 = lane_table_at(ltab, 4 * c1);
         } else {
-            c0 = lloyd_code16(y0);
-            c1 = lloyd_code16(y1);
-            q0 = centroid16_abs(c0);
-            q1 = centroid16_abs(c1);
+            int m0, m1;
+            c0 = lloyd_cell16(y0, ttab, m0);
+            c1 = lloyd_cell16(y1, ttab, m1);
+            q0 = lane_table_at(ltab, 4 * m0);
+            q1 = lane_table_at(ltab, 4 * m1);
         }
         const float gam = __fdiv_rn(1.0f, sqrt_rn(wave_tree_sum(__fadd_rn(__fmul_rn(q0, q0), __fmul_rn(q1, q1)), lane)));
         r.m0 = f2h(n);
@@ -286,14 +325,25 @@ __device__ inline Record quantize_record(const TokenHead &in, int lane)
             amax = fmaxf(amax, lane_xor_n(amax, s, lane));
         const uint16_t sh = f2h(__fdiv_rn(amax, 448.0f));
         const float sc = h2f_q(sh);
-        r.c0 = (sc == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x0, sc));
-        r.c1 = (sc == 0.0f) ? 0u : e4m3_rne_sat(__fdiv_rn(x1, sc));
+        // codes of x / s from the product with 1 / s, the exact division
+        // where the product lies near a rounding boundary
+        const float rsc = __fdiv_rn(1.0f, sc);
+        const float p0 = __fmul_rn(x0, rsc), p1 = __fmul_rn(x1, rsc);
+        uint32_t k0 = e4m3_code(p0), k1 = e4m3_code(p1);
+        if (__builtin_expect(__any(e4m3_near_boundary(p0) || e4m3_near_boundary(p1)), 0)) {
+            if (e4m3_near_boundary(p0))
+                k0 = e4m3_code(__fdiv_rn(x0, sc));
+            if (e4m3_near_boundary(p1))
+                k1 = e4m3_code(__fdiv_rn(x1, sc));
+        }
+        r.c0 = (sc == 0.0f) ? 0u : k0;
+        r.c1 = (sc == 0.0f) ? 0u : k1;
         r.m0 = sh;
         r.m1 = 0;
     }
 
     // -------------------------------------------------------------- values
-    const float v0 = h2f_q(in.v0), v1 = h2f_q(in.v1);
+    const float v0 = h2f_q((uint16_t)in.v0), v1 = h2f_q((uint16_t)in.v1);
     float mn = fminf(fminf(__int_as_float(0x7F800000), v0), v1);
     float mx = fmaxf(fmaxf(__int_as_float(0xFF800000), v0), v1);
 #pragma unroll
@@ -305,13 +355,18 @@ __device__ inline Record quantize_record(const TokenHead &in, int lane)
     const float zero = h2f_q(zh);
     const uint16_t sch = f2h(__fdiv_rn(__fsub_rn(mx, mn), 15.0f));
     const float sc = h2f_q(sch);
-    auto vcode = [&](float v) -> uint32_t {
-        if (sc == 0.0f)
-            return 0u;
-        float q = rintf(__fdiv_rn(__fsub_rn(v, zero), sc));
-        return (q > 0.0f) ? ((q >= 15.0f) ? 15u : (uint32_t)q) : 0u;
-    };
-    const uint32_t vc0 = vcode(v0), vc1 = vcode(v1);
+    // codes clamp(rint((v - zero) / s), 0, 15): the product with 1 / s, the
+    // exact division near a tie
+    const float rs = __fdiv_rn(1.0f, sc);
+    const float g0 = __fmul_rn(__fsub_rn(v0, zero), rs), g1 = __fmul_rn(__fsub_rn(v1, zero), rs);
+    float r0 = rintf(g0), r1 = rintf(g1);
+    if (__builtin_expect(__any(code_near_tie(g0, r0) || code_near_tie(g1, r1)), 0)) {
+        if (code_near_tie(g0, r0))
+            r0 = rintf(__fdiv_rn(__fsub_rn(v0, zero), sc));
+        if (code_near_tie(g1, r1))
+            r1 = rintf(__fdiv_rn(__fsub_rn(v1, zero), sc));
+    }
+    const uint32_t vc0 = (sc == 0.0f) ? 0u : code_clamp(r0), vc1 = (sc == 0.0f) ? 0u : code_clamp(r1);
     const uint32_t o0 = lane_xor<1>(vc0, lane), o1 = lane_xor<1>(vc1, lane);
     // even lane: byte l/2 = (d=l | d=l+1); odd lane: byte 32 + l/2 = (d=l+63 | d=l+64)
     r.vpos = (lane & 1) ? (32 + (lane >> 1)) : (lane >> 1);

@@ -84,94 +84,6 @@ __device__ inline void group_wht(float (&x)[kPer], int lane)
             }
 }
 
-// Lloyd-Max cells by binary search over the sorted thresholds: the cell is
-// #{j : y >= tau_j} either way (a NaN compares false at every step and lands
-// in cell 0), in three comparisons for 8 levels and four for 16 instead of
-// seven and fifteen.  Thresholds and levels come from lane tables through
-// ds_bpermute (lane l holds tau_(l % 16), and level l % 8 or, for 16 levels,
-// the magnitude |c16_(8 + l % 8)|); the probe moves by integer steps, so
-// there is no select of floating-point constants (the compiler turned
-// nested ones into branches) and no register per constant.
-template <int NL> __device__ inline uint32_t threshold_lane_table(int lane)
-{
-    const int k = lane & 15;
-    float v = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NL - 1; ++j)
-        if (k == j)
-            v = (NL == 8) ? kThreshold[j] : kThreshold16[j];
-    return __float_as_uint(v);
-}
-template <int NL> __device__ inline uint32_t level_lane_table(int lane)
-{
-    const int k = lane & 7;
-    float v = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (k == j)
-            v = (NL == 8) ? kCentroid[j] : kCentroid16[8 + j];
-    return __float_as_uint(v);
-}
-// entry byte_idx / 4 of a lane table
-__device__ inline float lane_table_at(uint32_t tab, int byte_idx)
-{
-    return __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(byte_idx, (int)tab));
-}
-__device__ inline int lloyd_cell8(float y, uint32_t ttab)
-{
-    const bool b2 = y >= kThreshold[3];
-    int i = b2 ? 4 * 5 : 4 * 1; // tau_(4 b2 + 1)
-    const bool b1 = y >= lane_table_at(ttab, i);
-    i += b1 ? 4 : -4; // tau_(2k), k = 2 b2 + b1: the cell pair {2k, 2k + 1}
-    const bool b0 = y >= lane_table_at(ttab, i);
-    return (i >> 2) + (b0 ? 1 : 0);
-}
-// m: the rank of |c16_c| from zero (c - 8 for c >= 8, 7 - c below: the
-// three low bits of c, inverted when bit 3 is clear, since the codebook is
-// symmetric)
-__device__ inline int lloyd_cell16(float y, uint32_t ttab, int &m)
-{
-    const bool b3 = y >= kThreshold16[7];
-    int i = b3 ? 4 * 11 : 4 * 3; // tau_(8 b3 + 3)
-    const bool b2 = y >= lane_table_at(ttab, i);
-    i += b2 ? 8 : -8; // tau_(8 b3 + 4 b2 + 1)
-    const bool b1 = y >= lane_table_at(ttab, i);
-    i += b1 ? 4 : -4; // tau_(2k), k = 4 b3 + 2 b2 + b1: the cell pair {2k, 2k + 1}
-    const bool b0 = y >= lane_table_at(ttab, i);
-    const int c = (i >> 2) + (b0 ? 1 : 0);
-    m = (c & 7) ^ (b3 ? 0 : 7);
-    return c;
-}
-
-// OCP E4M3 code of binary32 q (round to nearest even, saturation to +-448,
-// NaN -> 0x7F; the encoding of the FP8 keys), without branches: in the
-// normal range the bit pattern is rounded at bit 20 (ties to even) and the
-// exponent rebiased by 127 - 7; below 2^-6 the code is rint(|q| * 2^9).
-__device__ inline uint32_t e4m3_code(float q)
-{
-    const uint32_t u = __float_as_uint(q), a = u & 0x7FFFFFFFu;
-    const uint32_t rn = (a + 0x7FFFFu + ((a >> 20) & 1u) - (120u << 23)) >> 20;
-    const uint32_t cn = rn < 0x7Eu ? rn : 0x7Eu;
-    const uint32_t cs = (uint32_t)rintf(__fmul_rn(__uint_as_float(a), 512.0f));
-    const uint32_t c = (a < 0x3C800000u) ? cs : cn;
-    return (a > 0x7F800000u) ? 0x7Fu : (((u >> 24) & 0x80u) | c);
-}
-
-// q = x * (1 / s) (two roundings) is within 2^-23 |x / s| of the correctly
-// rounded quotient, i.e. two units in its last place: its E4M3 code can
-// differ from the quotient's only where q lies that close to a rounding
-// boundary: the 20 discarded bits near 0x80000 (normal range), |q| * 2^9
-// near a half-integer (below 2^-6; a 2^-20 error there).  The margins are
-// 4 units and 2^-16.
-__device__ inline bool e4m3_near_boundary(float q)
-{
-    const uint32_t a = __float_as_uint(q) & 0x7FFFFFFFu;
-    const float t = __fmul_rn(__uint_as_float(a), 512.0f);
-    const bool sub = fabsf(t - rintf(t)) > 0.5f - 0x1p-16f;
-    const bool nrm = ((a & 0xFFFFFu) - 0x7FFFCu) < 9u;
-    return (a < 0x3C800000u) ? sub : nrm;
-}
-
 // 16 binary16 values (coordinates 16j .. 16j + 15 of a row) as 8 words
 __device__ inline void load_run(uint32_t (&w)[kPer / 2], const uint16_t *p, bool aligned)
 {
@@ -186,18 +98,6 @@ __device__ inline void load_run(uint32_t (&w)[kPer / 2], const uint16_t *p, bool
             w[i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
     }
 }
-
-// Value codes clamp(rint(a / s), 0, 15) with a / s the correctly rounded
-// binary32 quotient (s > 0).  The product a * (1 / s) of two roundings
-// differs from that quotient by under 3e-6 for |a / s| <= 16, so where no
-// integer + 1/2 lies within 4e-6 of it both round to the same integer;
-// near such a point (rarely) the exact division decides, for the whole
-// wavefront at once.  The test reuses the rounding: q is within 4e-6 of a
-// half-integer exactly when |q - rint(q)| (an exact difference) exceeds
-// 1/2 - 4e-6.  Outside [-0.5, 15.5] the clamp decides either way.
-__device__ inline bool code_near_tie(float q, float r) { return fabsf(q - r) > 0.5f - 4e-6f; }
-// clamp to [0, 15] of an integral value; NaN -> 0 (fmaxf returns the number)
-__device__ inline uint32_t code_clamp(float r) { return (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f); }
 
 template <int PRESET>
 __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
@@ -283,19 +183,19 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
         group_wht(x, lane);
         const float rr = __fdiv_rn(1.0f, __fmul_rn(quant::sqrt_rn(128.0f), n));
         constexpr int NL = (PRESET == kPresetK3V4) ? 8 : 16;
-        const uint32_t ttab = threshold_lane_table<NL>(lane), ltab = level_lane_table<NL>(lane);
+        const uint32_t ttab = quant::threshold_lane_table<NL>(lane), ltab = quant::level_lane_table<NL>(lane);
         int c[kPer];
         float q[kPer];
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
             const float y = __fmul_rn(x[m], rr);
             if constexpr (PRESET == kPresetK3V4) {
-                c[m] = lloyd_cell8(y, ttab);
-                q[m] = lane_table_at(ltab, 4 * c[m]);
+                c[m] = quant::lloyd_cell8(y, ttab);
+                q[m] = quant::lane_table_at(ltab, 4 * c[m]);
             } else {
                 int r;
-                c[m] = lloyd_cell16(y, ttab, r);
-                q[m] = lane_table_at(ltab, 4 * r);
+                c[m] = quant::lloyd_cell16(y, ttab, r);
+                q[m] = quant::lane_table_at(ltab, 4 * r);
             }
         }
         const float gam = __fdiv_rn(1.0f, quant::sqrt_rn(group_tree_sumsq(q, lane)));
@@ -388,15 +288,15 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float q = __fmul_rn(x[4 * i + e], rsc);
-                w[i] |= e4m3_code(q) << (8 * e);
-                doubt |= e4m3_near_boundary(q);
+                w[i] |= quant::e4m3_code(q) << (8 * e);
+                doubt |= quant::e4m3_near_boundary(q);
             }
         }
         if (__builtin_expect(__any(doubt), 0)) {
 #pragma unroll
             for (int m = 0; m < kPer; ++m)
-                if (e4m3_near_boundary(__fmul_rn(x[m], rsc))) {
-                    const uint32_t c = e4m3_code(__fdiv_rn(x[m], sc));
+                if (quant::e4m3_near_boundary(__fmul_rn(x[m], rsc))) {
+                    const uint32_t c = quant::e4m3_code(__fdiv_rn(x[m], sc));
                     w[m / 4] = (w[m / 4] & ~(0xFFu << (8 * (m % 4)))) | (c << (8 * (m % 4)));
                 }
         }
@@ -437,13 +337,13 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
     for (int m = 0; m < kPer; ++m) {
         const float q = __fmul_rn(__fsub_rn(v[m], zero), rs);
         qr[m] = rintf(q);
-        near |= code_near_tie(q, qr[m]);
+        near |= quant::code_near_tie(q, qr[m]);
     }
     if (__builtin_expect(__any(near), 0)) {
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
             const float q = __fmul_rn(__fsub_rn(v[m], zero), rs);
-            if (code_near_tie(q, qr[m]))
+            if (quant::code_near_tie(q, qr[m]))
                 qr[m] = rintf(__fdiv_rn(__fsub_rn(v[m], zero), sc));
         }
     }
@@ -453,8 +353,8 @@ __global__ __launch_bounds__(kStoreThreads) void store_kernel(StoreArgs a)
         for (int i = 0; i < kPer / 2; ++i) {
             uint32_t c0 = 0u, c1 = 0u;
             if (sc != 0.0f) {
-                c0 = code_clamp(qr[2 * i]);
-                c1 = code_clamp(qr[2 * i + 1]);
+                c0 = quant::code_clamp(qr[2 * i]);
+                c1 = quant::code_clamp(qr[2 * i + 1]);
             }
             vb[val_byte_offset(tb, 8 * j + i)] = (uint8_t)(c0 | (c1 << 4));
         }

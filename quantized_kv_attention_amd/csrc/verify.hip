@@ -1580,8 +1580,8 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     }
 
     // 3. fused store of this work-group's share of the new tokens, spread
-    //    over the eight wavefronts; complete before any tile holding them is
-    //    loaded
+    //    over the eight wavefronts; complete (the wait for the query rows
+    //    below) before any tile holding them is loaded
     if (wn0 < wn1) {
         for (int t = wn0 + wave; t < wn1; t += 2 * kW) {
             const int t2 = t + kW;
@@ -1608,8 +1608,6 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                     quant::store_record<PRESET>(blk, t & 15, r1, lane);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
     }
     // 4. state
     int erow[NQT];
@@ -1626,7 +1624,12 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     uint32_t *claim_ctr = reinterpret_cast<uint32_t *>(lds + kQRegion - 16);
     static_assert(RP * kQStride * 2 <= kQRegion - 16, "claim counter");
 
-    wait_ring<LPT>(issued); // this wavefront's query loads have landed
+    // this wavefront's query loads have landed; a wavefront that stored new
+    // tokens waits for its stores too, so after the barrier every new token
+    // is in memory (the ring loads of tiles that hold them come later)
+    wait_ring<LPT>(issued);
+    if (wn0 + wave < wn1)
+        wait_vm<0>();
     lds_barrier();
 
     // 5. scale and round to binary16 (thread t: 16 coordinates of row t / 8)
