@@ -2002,9 +2002,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     // ------------------------------------------- output or partial state
     auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
     if (a.nsplit > 1 && aa == 0 && h == 0 && tile0 + mq < a.nrt) {
-        float *pm = reinterpret_cast<float *>(&a.part_ml[part_slot(tile0 + mq) + lrow]);
-        __builtin_nontemporal_store(M, pm);
-        __builtin_nontemporal_store(Ls, pm + 1);
+        a.part_ml[part_slot(tile0 + mq) + lrow] = make_float2(M, Ls);
     }
     if (a.nsplit == 1 && Ls == 0.0f) {
 #pragma unroll
@@ -2031,10 +2029,13 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             *reinterpret_cast<float4 *>(dst + 4 * (8 * aa + 4 * h + j)) = make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
         return;
     }
-    _Float16 *po = a.part_o + (part_slot(tile0 + mq) + lrow) * kD;
+    // The 16 coordinates are consecutive (32 B): two 16-byte stores, write-
+    // back cached so that the halves meet in L2 before memory (8-byte
+    // streaming stores wrote 2.3x the partial-state bytes to HBM).
+    _Float16 *po = a.part_o + (part_slot(tile0 + mq) + lrow) * kD + 4 * (8 * aa + 4 * h);
+    uint32_t w8[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t w2[2];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             // binary16 range, NaN kept
@@ -2043,10 +2044,10 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             float r2 = fminf(fmaxf(x1, -65504.0f), 65504.0f);
             p = (x0 == x0) ? p : x0;
             r2 = (x1 == x1) ? r2 : x1;
-            w2[q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
+            w8[2 * j + q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
         }
-        __builtin_nontemporal_store(u32x2{w2[0], w2[1]}, reinterpret_cast<u32x2 *>(po + 4 * (8 * aa + 4 * h + j)));
-    }
+    reinterpret_cast<u32x4 *>(po)[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
+    reinterpret_cast<u32x4 *>(po)[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
 }
 
 // Merge of the key ranges of each (b, hk, row tile): out = sum_s w_s O_s /
