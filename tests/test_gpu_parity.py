@@ -115,13 +115,10 @@ def _binary16_up_to(a):
     return np.concatenate([mags, -mags])
 
 
-@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
-def test_store_every_binary16_value(preset):
-    """Every finite binary16 below each of a range of maxima (subnormal, tiny,
-    near 1, 448, the binary16 maximum): each token-head holds its maximum and
-    127 values at most as large, so the FP8 key codes meet every quotient
-    x / s that their scale s allows, and the value codes every (v - zero) / s
-    of a wide range (rounding boundaries and ties included)."""
+def _every_binary16_rows():
+    """Token-head rows [T, 128] (T = 3168) holding every finite binary16 below
+    each of a range of maxima (subnormal, tiny, near 1, 448, the binary16
+    maximum): each row is its maximum and 127 values at most as large."""
     maxima = [2.0**-24, 2.0**-17, 2.0**-14, 1e-3, 0.1, 1.0, 1.5, np.pi, 100.0, 448.0, 1000.0, 3e4, 65504.0]
     rng = np.random.default_rng(5)
     rows = []
@@ -132,9 +129,17 @@ def test_store_every_binary16_value(preset):
             if len(chunk) < 127:
                 chunk = np.concatenate([chunk, rng.choice(xs, 127 - len(chunk))])
             rows.append(np.concatenate([[np.float16(a)], chunk]))
-    K = np.stack(rows).astype(np.float16)[:, None, :]
+    return np.stack(rows).astype(np.float16)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_store_every_binary16_value(preset):
+    """With these rows as keys and (reversed) as values, the FP8 key codes meet
+    every quotient x / s that their scale s allows, and the value codes every
+    (v - zero) / s of a wide range (rounding boundaries and ties included)."""
+    K = _every_binary16_rows()[:, None, :]
     V = np.ascontiguousarray(K[:, :, ::-1])
-    T = len(rows)
+    T = K.shape[0]
     si = np.zeros(T, np.int32)
     po = np.arange(T, dtype=np.int32)
     print("store every binary16", PNAME[preset], T, "token-heads", flush=True)
@@ -406,6 +411,36 @@ def test_store_verify_fused(preset, shape):
     got_cache = cache.buffer.cpu().numpy()
     assert np.array_equal(got_cache, ref_cache), "%d bytes differ" % int((got_cache != ref_cache).sum())
     assert_close(out.cpu().numpy(), ref, what="fused " + str(shape))
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+def test_store_verify_fused_every_binary16_value(preset):
+    """The fused store (one wavefront per token-head) on the every-binary16
+    rows as the new tokens of 396 sequences (64 query rows each): the same
+    cache bytes as the oracle's store."""
+    rows = _every_binary16_rows()
+    N, Hk, Hq, S = 8, 1, 8, 16
+    B = rows.shape[0] // N
+    cfg = _small(preset, N=N, B=B, Hq=Hq, Hk=Hk, S=S)
+    inp = synth.make_inputs(cfg)
+    Kn = np.ascontiguousarray(rows[:B * N].reshape(B, N, 1, 128).transpose(1, 0, 2, 3))  # [N, B, Hk, 128]
+    Vn = np.ascontiguousarray(Kn[..., ::-1])
+    lens = np.full(B, S, np.int32)
+    print("store_verify every binary16", PNAME[preset], B, "sequences", flush=True)
+    si0, po0 = _token_lists_ragged([S - N] * B)
+    si1, po1 = _token_lists_ragged([S] * B, start_from_end=N)
+    ref = np.zeros(oracle.cache_bytes(preset, B, Hk, S), np.uint8)
+    oracle.store(preset, ref, B, Hk, S, _rows_at(inp["K"], si0, po0), _rows_at(inp["V"], si0, po0), si0, po0)
+    oracle.store(preset, ref, B, Hk, S, np.ascontiguousarray(Kn[po1 - (S - N), si1]),
+                 np.ascontiguousarray(Vn[po1 - (S - N), si1]), si1, po1)
+    cache = tq.Cache(preset, B, Hk, S)
+    tq.tqkv_store(cache, to_dev(_rows_at(inp["K"], si0, po0)), to_dev(_rows_at(inp["V"], si0, po0)),
+                  to_dev(si0), to_dev(po0))
+    out = tq.tqkv_store_verify(cache, to_dev(Kn), to_dev(Vn), to_dev(inp["Q"]), to_dev(lens), N, Hq, True)
+    torch.cuda.synchronize()
+    assert out.shape == (N, B, Hq, 128)
+    got = cache.buffer.cpu().numpy()
+    assert np.array_equal(got, ref), "%d bytes differ" % int((got != ref).sum())
 
 
 # ------------------------------------------------ units of at most 8 rows ---
