@@ -1728,14 +1728,17 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
         return *reinterpret_cast<const half8_t *>(qrow + 32 * qt * kQStride + 8 * ks);
     };
     floatx16 acc[4][NQT];
-    float m[NQT], msub[NQT], thr[NQT], ls[NQT], zs[NQT];
+    float m[NQT], msub[NQT], thr[NQT];
+    // row sums on the matrix core: rows 2qt and 2qt + 1 of `sums` (registers
+    // 2qt, 2qt + 1 of the lanes of half 0) are sum_t P_t and sum_t P_t zero_t
+    // of row tile qt, accumulated as A P with A's row 2qt all ones and row
+    // 2qt + 1 the tokens' zeros
+    floatx16 sums = floatx16{0};
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
         m[qt] = -__builtin_inff();
         msub[qt] = 0.0f;
         thr[qt] = -__builtin_inff();
-        ls[qt] = 0.0f;
-        zs[qt] = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
             acc[dt][qt] = floatx16{0};
@@ -1755,6 +1758,15 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
         sub_hl[qt] = 0u;
+    // A operand of the sums of row tile qt: lane column 2qt all ones, lane
+    // column 2qt + 1 the zeros of its tokens (one select per dword)
+    uint32_t sum_ones[NQT];
+    bool sum_zlane[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+        sum_ones[qt] = (col == 2 * qt) ? 0x3C003C00u : 0u;
+        sum_zlane[qt] = col == 2 * qt + 1;
+    }
     // tile i: S = K Q^T, the lazy online-softmax rescale (the running max
     // moves only when a score exceeds it by more than kRescaleSlack; an
     // unset max takes the tile's maximum), P = exp2(S - m) in binary16, the
@@ -1838,8 +1850,8 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
                     acc[dt][qt] *= alpha;
-                ls[qt] *= alpha;
-                zs[qt] *= alpha;
+                sums[2 * qt] *= alpha;
+                sums[2 * qt + 1] *= alpha;
                 m[qt] = mnew;
                 msub[qt] = snew;
                 sub_hl[qt] = split_sub(snew);
@@ -1865,7 +1877,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
-                H8 Bp;
+                H8 Bp, Pr, As;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     // (vector elements are copied to scalars first: a bit cast
@@ -1875,10 +1887,11 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                     const float p0 = __builtin_amdgcn_exp2f(S[qt][8 * s2 + 2 * j]);
                     const float p1 = __builtin_amdgcn_exp2f(S[qt][8 * s2 + 2 * j + 1]);
                     const half2_t ph = half2_t{(_Float16)p0, (_Float16)p1};
-                    ls[qt] = __builtin_amdgcn_fdot2(ph, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls[qt], false);
-                    zs[qt] = __builtin_amdgcn_fdot2(ph, __builtin_bit_cast(half2_t, vzj), zs[qt], false);
+                    Pr.u[j] = __builtin_bit_cast(uint32_t, ph);
+                    As.u[j] = sum_zlane[qt] ? vzj : sum_ones[qt];
                     Bp.u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vsj));
                 }
+                sums = __builtin_amdgcn_mfma_f32_32x32x16_f16(As.h, Pr.h, sums, 0, 0, 0);
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
                     acc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(value_operand(vr.v, dt, s2), Bp.h, acc[dt][qt],
@@ -1933,7 +1946,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     __syncthreads(); // every wavefront is done with the ring and the query rows
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-        const float l2 = halves_sum(ls[qt]), z2 = halves_sum(zs[qt]);
+        const float l2 = sums[2 * qt], z2 = sums[2 * qt + 1];
         if (h == 0)
             sbuf[wave * RP + 32 * qt + col] = make_float4(m[qt], l2, z2, 0.0f);
     }
