@@ -31,13 +31,14 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(extra_flags=()) -> str:
-    """Compile every HIP source into libtqkv.so next to this file (always rebuilds)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
+def build(extra_flags=(), out=LIB) -> str:
+    """Compile every HIP source into `out` (libtqkv.so next to this file by
+    default; always rebuilds)."""
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -45,6 +45,44 @@
 #include <type_traits>
 
 namespace tqkv {
+
+// Phase trace of verify_wide_kernel, compiled only with -DTQKV_PHASE_TRACE
+// (a separate library, quantized_kv_attention_amd/phase_trace.py): every
+// wavefront keeps the low 32 bits of s_memrealtime stamps (100 MHz; the
+// host takes differences modulo 2^32) in registers and stores
+// them after its key loop and at its end, so the stamps add no memory
+// operation to the loop's vmcnt bookkeeping.  Slots: 0 entry, 1 query rows
+// landed, 2 key loop start, 3 + 3i .. 5 + 3i step i < 4 (tile landed, tile
+// max done, step issued), 15 loop end, 16 / 17 fused store start / stores
+// issued, 18 merge done, 19 end, 20 = 1 when the work-group stores new
+// tokens, 22 / 23 s_memtime (shader clock) at loop start / end.
+#ifdef TQKV_PHASE_TRACE
+constexpr int kTraceWGs = 4096, kTraceSlots = 24;
+__device__ uint32_t g_phase_trace[kTraceWGs * 8 * kTraceSlots];
+#define TQKV_TRACE_DECL uint32_t trv_[kTraceSlots] = {}
+#define TQKV_STAMP(k) (trv_[(k)] = (uint32_t)__builtin_amdgcn_s_memrealtime())
+#define TQKV_CLOCK(k) (trv_[(k)] = (uint32_t)__builtin_amdgcn_s_memtime())
+#define TQKV_SET(k, v) (trv_[(k)] = (v))
+#define TQKV_STEP_STAMP(i, p)                                                                                         \
+    do {                                                                                                               \
+        _Pragma("unroll") for (int kk_ = 0; kk_ < 4; ++kk_) if ((i) == kk_) TQKV_STAMP(3 + 3 * kk_ + (p));             \
+    } while (0)
+#define TQKV_TRACE_STORE(lo, hi)                                                                                       \
+    do {                                                                                                               \
+        if (lane == 0 && blockIdx.x < kTraceWGs) {                                                                     \
+            _Pragma("unroll") for (int k_ = (lo); k_ < (hi); ++k_)                                                     \
+                g_phase_trace[((size_t)blockIdx.x * 8 + wave) * kTraceSlots + k_] = trv_[k_];                          \
+        }                                                                                                              \
+    } while (0)
+#else
+#define TQKV_TRACE_DECL
+#define TQKV_STAMP(k) ((void)0)
+#define TQKV_CLOCK(k) ((void)0)
+#define TQKV_SET(k, v) ((void)0)
+#define TQKV_STEP_STAMP(i, p) ((void)0)
+#define TQKV_TRACE_STORE(lo, hi) ((void)0)
+#endif
+
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -1461,6 +1499,8 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, col = lane & 31;
+    TQKV_TRACE_DECL;
+    TQKV_STAMP(0);
     int item = blockIdx.x;
     if ((gridDim.x & 7) == 0)
         item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
@@ -1582,7 +1622,9 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     // 3. fused store of this work-group's share of the new tokens, spread
     //    over the eight wavefronts; complete (the wait for the query rows
     //    below) before any tile holding them is loaded
+    TQKV_SET(20, wn0 < wn1 ? 1u : 0u);
     if (wn0 < wn1) {
+        TQKV_STAMP(16);
         for (int t = wn0 + wave; t < wn1; t += 2 * kW) {
             const int t2 = t + kW;
             quant::TokenHead x = nx1, x2 = nx2;
@@ -1608,6 +1650,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                     quant::store_record<PRESET>(blk, t & 15, r1, lane);
             }
         }
+        TQKV_STAMP(17);
     }
     // 4. state
     int erow[NQT];
@@ -1630,6 +1673,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     wait_ring<LPT>(issued);
     if (wn0 + wave < wn1)
         wait_vm<0>();
+    TQKV_STAMP(1);
     lds_barrier();
 
     // 5. scale and round to binary16 (thread t: 16 coordinates of row t / 8)
@@ -1721,6 +1765,8 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             issue(tq[j], ring_lds + j * kSlotBytes);
             ++issued;
         }
+    TQKV_STAMP(2);
+    TQKV_CLOCK(22);
     // the B operand of k-step ks of row tile qt: coordinates 64h + 8ks + 0..7
     // of this lane's query row 32qt + col, read from LDS when needed
     const _Float16 *qrow = qs + col * kQStride + 64 * h;
@@ -1780,6 +1826,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             wait_vm<(DEPTH - 1) * LPT>();
         else
             wait_ring<LPT>(issued - i - 1);
+        TQKV_STEP_STAMP(i, 0);
         const uint8_t *slot = ring + (i % DEPTH) * kSlotBytes;
         KeyRegs<PRESET> kr;
         read_keys<PRESET>(kr, slot, lane);
@@ -1858,6 +1905,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                 thr[qt] = (mnew == -__builtin_inff()) ? -__builtin_inff() : kRescaleSlack;
             }
         }
+        TQKV_STEP_STAMP(i, 1);
         ValRegs vr;
         read_values<PRESET>(vr, slot, lane);
         if constexpr (MASKED) {
@@ -1928,14 +1976,20 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     while (tq[0] < min(wt1, tmask)) {
         const uint32_t c = claim();
         step(i, tq[0], std::false_type{});
+        TQKV_STEP_STAMP(i, 2);
         advance(c);
     }
     while (tq[0] < wt1) {
         const uint32_t c = claim();
         step(i, tq[0], std::true_type{});
+        TQKV_STEP_STAMP(i, 2);
         advance(c);
     }
 
+    TQKV_STAMP(15);
+    TQKV_CLOCK(23);
+    TQKV_TRACE_STORE(0, 18);
+    TQKV_TRACE_STORE(20, 24);
     // ---------------------------------------------------------------- merge
     // Eight states per row (one per wavefront, over different tokens):
     // first every (m, l, z), then the accumulators of wavefronts 4..7 and of
@@ -2011,6 +2065,7 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
         put_acc();
     __syncthreads();
     gather(0);
+    TQKV_STAMP(18);
 
     // ------------------------------------------- output or partial state
     auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
@@ -2024,6 +2079,8 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
             for (int k = 0; k < 4; ++k)
                 O[j][k] = __builtin_nanf("");
     }
+    TQKV_STAMP(19);
+    TQKV_TRACE_STORE(18, 20);
     // Outputs straight from the registers (no LDS staging): this thread's
     // row 32 mq + lrow, coordinates 4 (8 aa + 4h + j) + 0..3 for j = 0..3,
     // as four binary32 (the output) or four binary16 (a partial state).
@@ -2264,3 +2321,15 @@ hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const
 }
 
 } // namespace tqkv
+
+#ifdef TQKV_PHASE_TRACE
+// Copy the phase stamps of the last verify_wide_kernel launch to the host
+// (kTraceWGs x 8 wavefronts x kTraceSlots 32-bit words).  Trace builds only.
+extern "C" int tqkv_debug_phase_trace(void *host, size_t bytes)
+{
+    if (bytes > sizeof(tqkv::g_phase_trace))
+        return -1;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(tqkv::g_phase_trace), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0
+                                                                                                                  : -1;
+}
+#endif
