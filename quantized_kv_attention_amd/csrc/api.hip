@@ -148,6 +148,31 @@ constexpr int kPagedTilesPerGroup = 256;
 // per compute unit).
 int rows_per_group(int rows) { return row_tiles(rows) >= 2 ? 2 : 1; }
 
+// The 32-row work-groups for a plain k8v4 verify whose key ranges are short:
+// when a 64-row work-group would give each of its eight wavefronts at most
+// two 32-token tiles, the merge of its eight 64-row states through LDS
+// (512 KiB per compute unit) costs more than converting every FP8 key tile
+// twice in two 32-row work-groups with four wavefronts each (measured at the
+// PoC shape, 8192 tokens and 16 key ranges: 0.9 us per call less; from 4
+// tiles per wavefront on, and for the Lloyd-Max presets, whose table lookups
+// cost more per tile, the 64-row work-groups are as fast or faster).  A fused
+// store + verify keeps the 64-row work-groups, whose eight wavefronts
+// quantise the new tokens.  The split count is the one planned for 64-row
+// work-groups either way, so the workspace size does not depend on this
+// choice.
+int kernel_rows_per_group(const View &c, int rows, int splits, bool fused)
+{
+    const int nqt = rows_per_group(rows);
+    if (nqt != 2 || fused || c.preset != kPresetK8V4)
+        return nqt;
+    const long tiles = (c.max_seq + 31) / 32;
+    const long per_range = (tiles + splits - 1) / splits;
+    if (per_range > 2 * 8)
+        return nqt;
+    const long groups = (long)c.B * c.Hk * splits * row_tiles(rows);
+    return groups <= INT32_MAX ? 1 : nqt;
+}
+
 // Key-range partitions per (b, hk): one compute unit's worth of work-groups
 // per compute unit overall (two 32-row or one 64-row work-group), at least
 // one 32-token tile per wavefront.
@@ -333,7 +358,8 @@ int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q
     a.btab = v.btab;
     a.bstride = v.bstride;
     a.npages = v.npages;
-    if (launch_verify(v.preset, v.btab != nullptr, rows_per_group(R), R <= 8, a, s) != hipSuccess)
+    if (launch_verify(v.preset, v.btab != nullptr, kernel_rows_per_group(v, R, splits, fused), R <= 8, a, s) !=
+        hipSuccess)
         return TQKV_ERR_LAUNCH;
     return TQKV_OK;
 }

@@ -643,6 +643,20 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
 
     // ------------------------------------------------------------ prologue
+    // 0. fused store: the new tokens [tn0, L) of this unit that fall in this
+    //    work-group's key range; this wavefront's first two token-heads are
+    //    loaded now, so their memory latency overlaps the query and ring loads
+    const int tn0 = (a.Knew != nullptr) ? L - nq : L;
+    const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile); // this work-group's share
+    quant::TokenHead nx1{0, 0, 0, 0}, nx2{0, 0, 0, 0};
+    if (wn0 + wave < wn1) {
+        const int t = wn0 + wave, t2 = min(t + kWaves, wn1 - 1);
+        const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+        const size_t src2 = ((size_t)(qt0 + (t2 - tn0) * qts) * a.Hk + hk) * kD;
+        nx1 = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+        nx2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+    }
+
     // 1. The unit's raw query rows -> LDS, 1 KiB per load (2 fp32 or 4 fp16
     //    rows).  Padding rows re-read row 0 and are zeroed below.  Every
     //    wavefront queues these loads before any wavefront queues ring loads,
@@ -714,10 +728,8 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
             return (p >= 0 && p < a.npages) ? a.wbase + ((size_t)p * a.Hk + hk) * L_::kBlockBytes : nullptr;
         }
     };
-    // fused store: new tokens [tn0, L) of this unit; tiles holding them are
-    // loaded only after they have been stored (step 3)
-    const int tn0 = (a.Knew != nullptr) ? L - nq : L;
-    const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile); // this work-group's share
+    // tiles holding new tokens are loaded only after they have been stored
+    // (step 3)
     const int pre = min(kInitTiles, max(0, min(ntile, (tn0 - kt0 * kTile) / kTile)));
     for (; issued < pre; ++issued)
         issue(issued, ring_lds + issued * kSlotBytes);
@@ -729,13 +741,17 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     //    them.  (Work-groups of the other row tiles store the same tokens
     //    again: identical bytes.)
     if (wn0 < wn1) {
-        // two token-heads per wavefront at a time, both loaded up front
+        // two token-heads per wavefront at a time, both loaded up front (the
+        // first two at the kernel start)
         for (int t = wn0 + wave; t < wn1; t += 2 * kWaves) {
             const int t2 = t + kWaves;
-            const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
-            const size_t src2 = ((size_t)(qt0 + (min(t2, wn1 - 1) - tn0) * qts) * a.Hk + hk) * kD;
-            const quant::TokenHead x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
-            const quant::TokenHead x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+            quant::TokenHead x = nx1, x2 = nx2;
+            if (t != wn0 + wave) {
+                const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+                const size_t src2 = ((size_t)(qt0 + (min(t2, wn1 - 1) - tn0) * qts) * a.Hk + hk) * kD;
+                x = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+                x2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+            }
             uint8_t *blk = store_block(t);
             if (t2 < wn1) {
                 // both records first (two independent exchange chains the

@@ -204,8 +204,10 @@ def _envelope(inp, case):
 @pytest.mark.parametrize("rows", [64, 32, 8], ids=lambda r: "rows%d" % r)
 def test_verify_precision_envelope(preset, case, rows):
     """The envelope cases in each row path (64 rows: eight-wavefront
-    work-groups; 32: one row tile; 8: the transposed few-row path), with one
-    key range and with eight, against the oracle's tolerance."""
+    work-groups, except k8v4 with eight key ranges of at most 16 tiles, which
+    takes two 32-row work-groups; 32: one row tile; 8: the transposed few-row
+    path), with one key range and with eight, against the oracle's
+    tolerance."""
     N = {64: 8, 32: 4, 8: 1}[rows]
     cfg = _small(preset, N=N, S=1000, seed=31)
     inp = _envelope(synth.make_inputs(cfg), case)
