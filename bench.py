@@ -272,6 +272,21 @@ class Workload:
         torch.cuda.empty_cache()
 
 
+def verify_kernels(cfg, splits):
+    """The launches of one plain tqkv_verify call at this configuration, as
+    the library chooses them: two 32-row work-groups per compute unit for a
+    k8v4 verify with more than 32 query rows per KV head whose key ranges
+    hold at most 16 tiles of 32 tokens (verify_kernel), otherwise one 64-row
+    work-group for more than 32 rows (verify_wide_kernel) or 32-row ones;
+    then the key-range merge when there is more than one range."""
+    rows = cfg["Hq"] // cfg["Hk"] * cfg["N"]
+    tiles = (cfg["S"] + 31) // 32
+    per_range = (tiles + splits - 1) // splits
+    wide = rows > 32 and not (cfg["preset"] == 1 and per_range <= 16)
+    names = "verify_wide_kernel" if wide else "verify_kernel"
+    return names + (" + combine_kernel" if splits > 1 else "")
+
+
 def verify_entry(w, args):
     """us per call of the verify launch (auto splits and 8 splits), of the
     fused step, of a bulk store of every token, and the verify roofline."""
@@ -311,6 +326,7 @@ def verify_entry(w, args):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(w.name),
             "bytes_per_launch": kv_bytes + qo_bytes,
+            "kernel": "tqkv_verify: " + verify_kernels(c, tq.tqkv_verify_num_splits(w.caches[0], N, Hq, ns)),
             "mfma": {"flops_per_launch": flops, "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         },
@@ -443,7 +459,6 @@ def main():
 
     pages_ms = PAGES_FUSED_TRITON_MS.get(args.workload)
     roof = dict(entry["roofline"])
-    roof["kernel"] = "tqkv_verify: verify_wide_kernel (+ combine_kernel when splits > 1)"
     roof["measured_copy_GBps"] = round(copy_gbs, 1)
     roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
     rec = {
