@@ -87,6 +87,8 @@ def run(workload: str, fused: bool, calls: int = 40):
 
 def summarise(t: np.ndarray, title: str) -> str:
     n = int((t[:, :, 2] != 0).any(axis=1).sum())  # work-groups that reached the key loop
+    if n == 0:
+        return "%s: no work-group of verify_wide_kernel ran (the call took the 32-row work-groups)" % title
     t = t[:n]
     start = t[:, :, 0]
     ws0 = start.min(axis=1)

@@ -29,3 +29,9 @@ def test_summary_of_synthetic_stamps():
     # wavefront 7 starts 0.7 us after the work-group
     line7 = [x for x in text.splitlines() if x.strip().startswith("wavefront 7")][1]
     assert "start 0.70" in line7
+
+
+def test_summary_without_wide_work_groups():
+    # a call that ran no 64-row work-group leaves the stamps at zero
+    t = np.zeros((pt.WGS, 8, pt.SLOTS), np.int64)
+    assert "no work-group of verify_wide_kernel ran" in pt.summarise(t, "plain")
