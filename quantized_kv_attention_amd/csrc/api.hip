@@ -134,6 +134,10 @@ int view_of(const tqkv_paged_cache *c, View &v)
     return TQKV_OK;
 }
 
+// Longest key range (in 32-token tiles) that the 64-row work-groups run
+// with four wavefronts.
+constexpr long kWideFourTiles = 32;
+
 // Query rows per work-group: the rows of one KV head are cut into tiles of
 // 32 (one MFMA operand height), one work-group each.
 int row_tiles(int rows) { return (rows + 31) / 32; }
@@ -171,6 +175,18 @@ int kernel_rows_per_group(const View &c, int rows, int splits, bool fused)
         return nqt;
     const long groups = (long)c.B * c.Hk * splits * row_tiles(rows);
     return groups <= INT32_MAX ? 1 : nqt;
+}
+
+// Wavefronts of a 64-row work-group: four (one per SIMD, each taking a
+// quarter of the range's tiles, a four-state merge) when the key ranges are
+// short, eight (two per SIMD, an eight-state merge) otherwise.
+int wide_waves(const View &c, int splits)
+{
+    if (c.preset == kPresetK3V4)
+        return 8;
+    const long tiles = (c.max_seq + 31) / 32;
+    const long per_range = (tiles + splits - 1) / splits;
+    return per_range <= kWideFourTiles ? 4 : 8;
 }
 
 // Key-range partitions per (b, hk): one compute unit's worth of work-groups
@@ -358,8 +374,8 @@ int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q
     a.btab = v.btab;
     a.bstride = v.bstride;
     a.npages = v.npages;
-    if (launch_verify(v.preset, v.btab != nullptr, kernel_rows_per_group(v, R, splits, fused), R <= 8, a, s) !=
-        hipSuccess)
+    const int nqt = kernel_rows_per_group(v, R, splits, fused);
+    if (launch_verify(v.preset, v.btab != nullptr, nqt, wide_waves(v, splits), R <= 8, a, s) != hipSuccess)
         return TQKV_ERR_LAUNCH;
     return TQKV_OK;
 }

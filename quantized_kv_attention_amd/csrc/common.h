@@ -123,6 +123,7 @@ inline int combine_groups_per_row(int nsplit)
 
 // Launchers (defined next to their kernels).
 hipError_t launch_store(int preset, const StoreArgs &a, hipStream_t s);
-hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_verify(int preset, bool paged, int nqt, int wide_waves, bool transposed, const VerifyArgs &a,
+                         hipStream_t s);
 
 } // namespace tqkv

@@ -1493,10 +1493,11 @@ template <> struct WideRing<kPresetK3V4> { static constexpr int kDepth = 4; };
 template <> struct WideRing<kPresetK4V4> { static constexpr int kDepth = 3; };
 template <> struct WideRing<kPresetK8V4> { static constexpr int kDepth = 2; };
 
-template <int PRESET, bool PAGED>
-__global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
+template <int PRESET, bool PAGED, int kW>
+__global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
 {
-    constexpr int NQT = 2, RP = 64, kW = 8;
+    static_assert(kW == 4 || kW == 8, "wavefronts per work-group");
+    constexpr int NQT = 2, RP = 64;
     constexpr int LPT = Ring<PRESET, 1>::kLoads, DEPTH = WideRing<PRESET>::kDepth;
     constexpr int kSlotBytes = LPT * 1024;
     // query rows: raw, then the fp16 operand rows in place (resident)
@@ -1692,42 +1693,54 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     TQKV_STAMP(1);
     lds_barrier();
 
-    // 5. scale and round to binary16 (thread t: 16 coordinates of row t / 8)
+    // 5. scale and round to binary16 (thread t: 16 coordinates of row
+    //    t / 8, and with four wavefronts of row t / 8 + 32 as well); every
+    //    raw row is read before the binary16 rows overwrite them in place
     {
-        constexpr int CPT = 16, TPR = kD / CPT;
-        const int rr = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * CPT;
-        uint32_t qh[CPT / 2];
-        if (a.q_f16) {
-            const _Float16 *src = reinterpret_cast<const _Float16 *>(lds + rr * 256) + c0;
+        constexpr int CPT = 16, TPR = kD / CPT, NPASS = 512 / (64 * kW);
+        const int c0 = (threadIdx.x % TPR) * CPT;
+        uint32_t qh[NPASS][CPT / 2];
 #pragma unroll
-            for (int c = 0; c < CPT; c += 8) {
-                const half8_t x = *reinterpret_cast<const half8_t *>(src + c);
+        for (int ps = 0; ps < NPASS; ++ps) {
+            const int rr = (int)threadIdx.x / TPR + ps * (64 / NPASS);
+            if (a.q_f16) {
+                const _Float16 *src = reinterpret_cast<const _Float16 *>(lds + rr * 256) + c0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half2_t p = half2_t{(_Float16)((float)x[2 * j] * a.qscale),
-                                              (_Float16)((float)x[2 * j + 1] * a.qscale)};
-                    qh[c / 2 + j] = __builtin_bit_cast(uint32_t, p);
+                for (int c = 0; c < CPT; c += 8) {
+                    const half8_t x = *reinterpret_cast<const half8_t *>(src + c);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const half2_t p = half2_t{(_Float16)((float)x[2 * j] * a.qscale),
+                                                  (_Float16)((float)x[2 * j + 1] * a.qscale)};
+                        qh[ps][c / 2 + j] = __builtin_bit_cast(uint32_t, p);
+                    }
+                }
+            } else {
+                const float *src = reinterpret_cast<const float *>(lds + rr * 512) + c0;
+#pragma unroll
+                for (int c = 0; c < CPT; c += 4) {
+                    const float4 x = *reinterpret_cast<const float4 *>(src + c);
+                    qh[ps][c / 2] =
+                        __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale)});
+                    qh[ps][c / 2 + 1] =
+                        __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale)});
                 }
             }
-        } else {
-            const float *src = reinterpret_cast<const float *>(lds + rr * 512) + c0;
+            if (row0 + rr >= Rb) {
 #pragma unroll
-            for (int c = 0; c < CPT; c += 4) {
-                const float4 x = *reinterpret_cast<const float4 *>(src + c);
-                qh[c / 2] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale)});
-                qh[c / 2 + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale)});
+                for (int j = 0; j < CPT / 2; ++j)
+                    qh[ps][j] = 0u;
             }
         }
-        if (row0 + rr >= Rb) {
-#pragma unroll
-            for (int j = 0; j < CPT / 2; ++j)
-                qh[j] = 0u;
-        }
         lds_barrier();
-        uint32_t *dst = reinterpret_cast<uint32_t *>(qs + rr * kQStride + c0);
 #pragma unroll
-        for (int j = 0; j < CPT / 2; j += 4)
-            *reinterpret_cast<u32x4 *>(dst + j) = u32x4{qh[j], qh[j + 1], qh[j + 2], qh[j + 3]};
+        for (int ps = 0; ps < NPASS; ++ps) {
+            const int rr = (int)threadIdx.x / TPR + ps * (64 / NPASS);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(qs + rr * kQStride + c0);
+#pragma unroll
+            for (int j = 0; j < CPT / 2; j += 4)
+                *reinterpret_cast<u32x4 *>(dst + j) = u32x4{qh[ps][j], qh[ps][j + 1], qh[ps][j + 2], qh[ps][j + 3]};
+        }
         if (threadIdx.x == 0)
             *claim_ctr = (uint32_t)(wt0 + kW * DEPTH);
         lds_barrier();
@@ -1774,13 +1787,23 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
 
     // ------------------------------------------------------------ key loop
     // the rest of the ring prefill (after the fused store: tiles holding new
-    // tokens are loaded only once they are stored)
+    // tokens are loaded only once they are stored): the first tile now, if
+    // it is not in flight yet, the others from the first step, once its
+    // score products are issued (a load instruction waits at issue while the
+    // memory pipeline is full, which here it is: the first tiles of every
+    // wavefront and the query rows are still in flight)
+    auto prefill_rest = [&]() {
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j)
-        if (issued == j && tq[j] < wt1) {
-            issue(tq[j], ring_lds + j * kSlotBytes);
-            ++issued;
-        }
+        for (int j = 0; j < DEPTH; ++j)
+            if (issued == j && tq[j] < wt1) {
+                issue(tq[j], ring_lds + j * kSlotBytes);
+                ++issued;
+            }
+    };
+    if (issued == 0 && tq[0] < wt1) {
+        issue(tq[0], ring_lds);
+        ++issued;
+    }
     TQKV_STAMP(2);
     TQKV_CLOCK(22);
     // the B operand of k-step ks of row tile qt: coordinates 64h + 8ks + 0..7
@@ -1872,6 +1895,8 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                 S[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                     A, qop(qt, ks), (ks == 0 && !kLloydMax<PRESET>) ? floatx16{0} : S[qt], 0, 0, 0);
         }
+        if (i == 0)
+            prefill_rest();
         // FP8: each score column times its token's key scale, relative to
         // the subtrahend (Lloyd-Max: already in the MFMA chain); register v
         // holds token tok0 + 8h + 16 (v / 8) + v % 8
@@ -2007,10 +2032,11 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     TQKV_TRACE_STORE(0, 18);
     TQKV_TRACE_STORE(20, 24);
     // ---------------------------------------------------------------- merge
-    // Eight states per row (one per wavefront, over different tokens):
-    // first every (m, l, z), then the accumulators of wavefronts 4..7 and of
-    // 0..3 in two rounds through the same LDS area; wavefront w reduces
-    // C-register quad aa = w % 4 of row tile mq = w / 4.
+    // kW states per row (one per wavefront, over different tokens): first
+    // every (m, l, z), then the accumulators in rounds of four wavefronts
+    // through the same LDS area (eight wavefronts: 4..7, then 0..3);
+    // wavefront w reduces C-register quad aa = w % 4 of row tile w / 4
+    // (eight wavefronts) or of both row tiles (four).
     float4 *xbuf = reinterpret_cast<float4 *>(lds); // [w % 4][qt][aa][dt][lane]
     float4 *sbuf = reinterpret_cast<float4 *>(lds + kXBytes); // [w][row]: m, l, z
     __syncthreads(); // every wavefront is done with the ring and the query rows
@@ -2020,7 +2046,9 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
         if (h == 0)
             sbuf[wave * RP + 32 * qt + col] = make_float4(m[qt], l2, z2, 0.0f);
     }
-    const int mq = wave >> 2, aa = wave & 3, lrow = col;
+    constexpr int NMQ = 8 / kW; // row tiles this wavefront reduces
+    const int aa = wave & 3, lrow = col;
+    auto row_tile = [&](int mi) { return (kW == 8) ? (wave >> 2) : mi; };
     auto put_acc = [&]() {
         const int ww = wave & 3;
 #pragma unroll
@@ -2033,67 +2061,83 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
                         make_float4(acc[dt][qt][4 * a2], acc[dt][qt][4 * a2 + 1], acc[dt][qt][4 * a2 + 2],
                                     acc[dt][qt][4 * a2 + 3]);
     };
-    if (wave >= 4)
+    if (kW == 4 || wave >= 4)
         put_acc();
     __syncthreads();
-    float M = -__builtin_inff();
-    float4 st[kW];
+    float M[NMQ], Ls[NMQ], al[NMQ][kW], inv[NMQ];
+    float O[NMQ][4][4]; // [mi][j][dt]: row 32 mq + lrow, coordinate 4 (8 aa + 4h + j) + dt
 #pragma unroll
-    for (int w = 0; w < kW; ++w) {
-        st[w] = sbuf[w * RP + 32 * mq + lrow];
-        M = fmaxf(M, st[w].x);
+    for (int mi = 0; mi < NMQ; ++mi) {
+        const int mq = row_tile(mi);
+        float4 st[kW];
+        M[mi] = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+            st[w] = sbuf[w * RP + 32 * mq + lrow];
+            M[mi] = fmaxf(M[mi], st[w].x);
+        }
+        float Zs = 0.0f;
+        Ls[mi] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+            al[mi][w] = (st[w].x == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(st[w].x - M[mi]);
+            Ls[mi] = __builtin_fmaf(al[mi][w], st[w].y, Ls[mi]);
+            Zs = __builtin_fmaf(al[mi][w], st[w].z, Zs);
+        }
+        inv[mi] = (Ls[mi] != 0.0f) ? 1.0f / Ls[mi] : 0.0f;
+        const float zo = Zs * inv[mi];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                O[mi][j][dt] = zo;
     }
-    float al[kW], Ls = 0.0f, Zs = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-        al[w] = (st[w].x == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(st[w].x - M);
-        Ls = __builtin_fmaf(al[w], st[w].y, Ls);
-        Zs = __builtin_fmaf(al[w], st[w].z, Zs);
-    }
-    const float inv = (Ls != 0.0f) ? 1.0f / Ls : 0.0f;
-    const float zo = Zs * inv;
-    float O[4][4]; // [j][dt]: row 32 mq + lrow, coordinate 4 (8 aa + 4h + j) + dt
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            O[j][dt] = zo;
     // normalised output O = (sum_w al_w acc_w * 2^24 (even d) or 2^20 (odd
     // d) + Zs) / Ls: the value operand carried c * 2^-24 (even d) and
     // 16c * 2^-24 (odd d)
     auto gather = [&](int wbase) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int mi = 0; mi < NMQ; ++mi) {
+            const int mq = row_tile(mi);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float k = al[wbase + w] * (((dt & 1) ? 1048576.0f : 16777216.0f) * inv);
-                const float4 x = xbuf[(((w * NQT + mq) * 4 + aa) * 4 + dt) * 64 + lane];
-                O[0][dt] = __builtin_fmaf(k, x.x, O[0][dt]);
-                O[1][dt] = __builtin_fmaf(k, x.y, O[1][dt]);
-                O[2][dt] = __builtin_fmaf(k, x.z, O[2][dt]);
-                O[3][dt] = __builtin_fmaf(k, x.w, O[3][dt]);
+            for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float k = al[mi][wbase + w] * (((dt & 1) ? 1048576.0f : 16777216.0f) * inv[mi]);
+                    const float4 x = xbuf[(((w * NQT + mq) * 4 + aa) * 4 + dt) * 64 + lane];
+                    O[mi][0][dt] = __builtin_fmaf(k, x.x, O[mi][0][dt]);
+                    O[mi][1][dt] = __builtin_fmaf(k, x.y, O[mi][1][dt]);
+                    O[mi][2][dt] = __builtin_fmaf(k, x.z, O[mi][2][dt]);
+                    O[mi][3][dt] = __builtin_fmaf(k, x.w, O[mi][3][dt]);
+                }
             }
         }
     };
-    gather(4);
-    __syncthreads();
-    if (wave < 4)
-        put_acc();
-    __syncthreads();
+    if constexpr (kW == 8) {
+        gather(4);
+        __syncthreads();
+        if (wave < 4)
+            put_acc();
+        __syncthreads();
+    }
     gather(0);
     TQKV_STAMP(18);
 
     // ------------------------------------------- output or partial state
     auto part_slot = [&](int t) { return ((size_t)(unit * a.nrt + t) * a.nsplit + split) * 32; };
-    if (a.nsplit > 1 && aa == 0 && h == 0 && tile0 + mq < a.nrt) {
-        a.part_ml[part_slot(tile0 + mq) + lrow] = make_float2(M, Ls);
-    }
-    if (a.nsplit == 1 && Ls == 0.0f) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int mi = 0; mi < NMQ; ++mi) {
+        const int mq = row_tile(mi);
+        if (a.nsplit > 1 && aa == 0 && h == 0 && tile0 + mq < a.nrt) {
+            a.part_ml[part_slot(tile0 + mq) + lrow] = make_float2(M[mi], Ls[mi]);
+        }
+        if (a.nsplit == 1 && Ls[mi] == 0.0f) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                O[j][k] = __builtin_nanf("");
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    O[mi][j][k] = __builtin_nanf("");
+        }
     }
     TQKV_STAMP(19);
     TQKV_TRACE_STORE(18, 20);
@@ -2102,38 +2146,43 @@ __global__ __launch_bounds__(512, 1) void verify_wide_kernel(VerifyArgs a)
     // as four binary32 (the output) or four binary16 (a partial state).
     // (A staging round through LDS for whole-row stores cost 0.2-0.6 us
     // per PoC call more.)
-    if (tile0 + mq >= a.nrt)
-        return;
-    if (a.nsplit == 1) {
-        const int grow = row0 + 32 * mq + lrow;
-        if (grow >= Rb)
-            return;
-        const int n = row_token(grow), g = grow - n * a.G;
-        float *dst = a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD;
+#pragma unroll
+    for (int mi = 0; mi < NMQ; ++mi) {
+        const int mq = row_tile(mi);
+        if (tile0 + mq >= a.nrt)
+            continue;
+        if (a.nsplit == 1) {
+            const int grow = row0 + 32 * mq + lrow;
+            if (grow >= Rb)
+                continue;
+            const int n = row_token(grow), g = grow - n * a.G;
+            float *dst = a.out + ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4 *>(dst + 4 * (8 * aa + 4 * h + j)) =
+                    make_float4(O[mi][j][0], O[mi][j][1], O[mi][j][2], O[mi][j][3]);
+            continue;
+        }
+        // The 16 coordinates are consecutive (32 B): two 16-byte stores,
+        // write-back cached so that the halves meet in L2 before memory
+        // (8-byte streaming stores wrote 2.3x the partial-state bytes to HBM).
+        _Float16 *po = a.part_o + (part_slot(tile0 + mq) + lrow) * kD + 4 * (8 * aa + 4 * h);
+        uint32_t w8[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4 *>(dst + 4 * (8 * aa + 4 * h + j)) = make_float4(O[j][0], O[j][1], O[j][2], O[j][3]);
-        return;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                // binary16 range, NaN kept
+                const float x0 = O[mi][j][2 * q], x1 = O[mi][j][2 * q + 1];
+                float p = fminf(fmaxf(x0, -65504.0f), 65504.0f);
+                float r2 = fminf(fmaxf(x1, -65504.0f), 65504.0f);
+                p = (x0 == x0) ? p : x0;
+                r2 = (x1 == x1) ? r2 : x1;
+                w8[2 * j + q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
+            }
+        reinterpret_cast<u32x4 *>(po)[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
+        reinterpret_cast<u32x4 *>(po)[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
     }
-    // The 16 coordinates are consecutive (32 B): two 16-byte stores, write-
-    // back cached so that the halves meet in L2 before memory (8-byte
-    // streaming stores wrote 2.3x the partial-state bytes to HBM).
-    _Float16 *po = a.part_o + (part_slot(tile0 + mq) + lrow) * kD + 4 * (8 * aa + 4 * h);
-    uint32_t w8[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            // binary16 range, NaN kept
-            const float x0 = O[j][2 * q], x1 = O[j][2 * q + 1];
-            float p = fminf(fmaxf(x0, -65504.0f), 65504.0f);
-            float r2 = fminf(fmaxf(x1, -65504.0f), 65504.0f);
-            p = (x0 == x0) ? p : x0;
-            r2 = (x1 == x1) ? r2 : x1;
-            w8[2 * j + q] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p, (_Float16)r2});
-        }
-    reinterpret_cast<u32x4 *>(po)[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
-    reinterpret_cast<u32x4 *>(po)[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
 }
 
 // Merge of the key ranges of each (b, hk, row tile): out = sum_s w_s O_s /
@@ -2258,25 +2307,26 @@ template <int GPR> __global__ __launch_bounds__(256) void combine_kernel(VerifyA
 
 
 
-void launch_verify_wide(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
+template <int KW>
+void launch_verify_wide_w(int preset, bool paged, const VerifyArgs &a, hipStream_t s)
 {
     const int nwt = (a.nrt + 1) / 2;
-    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * nwt)), block(512);
+    const dim3 grid((unsigned)(a.B * a.Hk * a.nsplit * nwt)), block(64 * KW);
     if (preset == kPresetK3V4) {
         if (paged)
-            hipLaunchKernelGGL((verify_wide_kernel<kPresetK3V4, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK3V4, true, KW>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_wide_kernel<kPresetK3V4, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK3V4, false, KW>), grid, block, 0, s, a);
     } else if (preset == kPresetK4V4) {
         if (paged)
-            hipLaunchKernelGGL((verify_wide_kernel<kPresetK4V4, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK4V4, true, KW>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_wide_kernel<kPresetK4V4, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK4V4, false, KW>), grid, block, 0, s, a);
     } else {
         if (paged)
-            hipLaunchKernelGGL((verify_wide_kernel<kPresetK8V4, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK8V4, true, KW>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((verify_wide_kernel<kPresetK8V4, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((verify_wide_kernel<kPresetK8V4, false, KW>), grid, block, 0, s, a);
     }
 }
 
@@ -2309,10 +2359,13 @@ void launch_verify_rows(int preset, bool paged, const VerifyArgs &a, hipStream_t
 // 2: one work-group of 64 rows per compute unit, each tile dequantised once
 // for all 64 rows); transposed: the transposed-score path (nqt 1, at most 8
 // rows per unit)
-hipError_t launch_verify(int preset, bool paged, int nqt, bool transposed, const VerifyArgs &a, hipStream_t s)
+hipError_t launch_verify(int preset, bool paged, int nqt, int wide_waves, bool transposed, const VerifyArgs &a,
+                         hipStream_t s)
 {
-    if (nqt == 2)
-        launch_verify_wide(preset, paged, a, s);
+    if (nqt == 2 && wide_waves == 4)
+        launch_verify_wide_w<4>(preset, paged, a, s);
+    else if (nqt == 2)
+        launch_verify_wide_w<8>(preset, paged, a, s);
     else if (transposed && a.R <= 8)
         launch_verify_rows<1, true>(preset, paged, a, s);
     else

@@ -11,7 +11,7 @@
 
 namespace tqkv {
 hipError_t launch_store(int, const StoreArgs &, hipStream_t) { return hipSuccess; }
-hipError_t launch_verify(int, bool, int, bool, const VerifyArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_verify(int, bool, int, int, bool, const VerifyArgs &, hipStream_t) { return hipSuccess; }
 } // namespace tqkv
 
 #define CHECK(cond)                                                                                                    \

@@ -241,6 +241,24 @@ def test_verify_explicit_scale(preset, scale):
 
 
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("ns", [1, 2, 3, 9])
+def test_verify_long_key_ranges(preset, ns):
+    """64 rows per KV head over 2100 tokens (66 tiles): key ranges of 66, 33,
+    22 and 8 tiles, which run the 64-row work-groups with eight wavefronts
+    (long ranges, and every k3v4_nc range) or four (ranges of at most 32
+    tiles), and for plain k8v4 at 8 tiles the 32-row work-groups."""
+    cfg = _small(preset, N=8, B=1, Hq=16, Hk=2, S=2100)
+    inp = synth.make_inputs(cfg)
+    inp["seq_lens"] = np.array([2093], np.int32)  # a partial last tile
+    print("verify long ranges", PNAME[preset], ns, flush=True)
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, cfg["B"], cfg["Hk"], cfg["S"], inp["Q"], inp["seq_lens"], cfg["Hq"], True)
+    cache = gpu_store_all(cfg, inp)
+    assert tq.tqkv_verify_num_splits(cache, cfg["N"], cfg["Hq"], ns) == ns
+    assert_close(_gpu_verify(cache, cfg, inp, num_splits=ns), ref, what="num_splits=%d" % ns)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
 @pytest.mark.parametrize("shape", [
     dict(N=1, Hq=1, Hk=1, B=1, S=17),          # one row, partial block
     dict(N=1, Hq=32, Hk=8, B=3, S=100),        # plain decode, 4 rows per KV head
@@ -384,6 +402,8 @@ def _rows_at(X, si, po):
     dict(N=4, B=3, Hq=8, Hk=1, S=100, lens=(100, 37, 64), ns=1),  # 32 rows, one key range
     dict(N=8, B=1, Hq=8, Hk=1, S=8, lens=(8,), ns=0),             # the whole sequence is new
     dict(N=1, B=2, Hq=4, Hk=1, S=50, lens=(50, 17), ns=2),        # plain decode
+    dict(N=8, B=2, Hq=16, Hk=2, S=2100, lens=(2100, 1500), ns=1), # 66-tile key ranges (eight wavefronts)
+    dict(N=8, B=2, Hq=16, Hk=2, S=2100, lens=(2100, 1500), ns=3), # 22-tile key ranges (four, except k3v4_nc)
 ], ids=lambda s: "N%d_Hq%d_Hk%d_S%d_ns%d" % (s["N"], s["Hq"], s["Hk"], s["S"], s["ns"]))
 def test_store_verify_fused(preset, shape):
     """tqkv_store_verify writes the same cache bytes as tqkv_store and returns
