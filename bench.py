@@ -274,16 +274,19 @@ class Workload:
 
 def verify_kernels(cfg, splits):
     """The launches of one plain tqkv_verify call at this configuration, as
-    the library chooses them: two 32-row work-groups per compute unit for a
-    k8v4 verify with more than 32 query rows per KV head whose key ranges
-    hold at most 16 tiles of 32 tokens (verify_kernel), otherwise one 64-row
-    work-group for more than 32 rows (verify_wide_kernel) or 32-row ones;
-    then the key-range merge when there is more than one range."""
+    the library chooses them: one 64-row work-group per compute unit for more
+    than 32 query rows per KV head (verify_wide_kernel, four wavefronts for
+    k8v4 / k4v4_nc key ranges of at most 32 tiles of 32 tokens, eight
+    otherwise), 32-row work-groups (verify_kernel) for fewer rows; then the
+    key-range merge when there is more than one range."""
     rows = cfg["Hq"] // cfg["Hk"] * cfg["N"]
     tiles = (cfg["S"] + 31) // 32
     per_range = (tiles + splits - 1) // splits
-    wide = rows > 32 and not (cfg["preset"] == 1 and per_range <= 16)
-    names = "verify_wide_kernel" if wide else "verify_kernel"
+    if rows > 32:
+        waves = 4 if cfg["preset"] != 2 and per_range <= 32 else 8
+        names = "verify_wide_kernel (%d wavefronts)" % waves
+    else:
+        names = "verify_kernel"
     return names + (" + combine_kernel" if splits > 1 else "")
 
 

@@ -152,34 +152,17 @@ constexpr int kPagedTilesPerGroup = 256;
 // per compute unit).
 int rows_per_group(int rows) { return row_tiles(rows) >= 2 ? 2 : 1; }
 
-// The 32-row work-groups for a plain k8v4 verify whose key ranges are short:
-// when a 64-row work-group would give each of its eight wavefronts at most
-// two 32-token tiles, the merge of its eight 64-row states through LDS
-// (512 KiB per compute unit) costs more than converting every FP8 key tile
-// twice in two 32-row work-groups with four wavefronts each (measured at the
-// PoC shape, 8192 tokens and 16 key ranges: 0.9 us per call less; from 4
-// tiles per wavefront on, and for the Lloyd-Max presets, whose table lookups
-// cost more per tile, the 64-row work-groups are as fast or faster).  A fused
-// store + verify keeps the 64-row work-groups, whose eight wavefronts
-// quantise the new tokens.  The split count is the one planned for 64-row
-// work-groups either way, so the workspace size does not depend on this
-// choice.
-int kernel_rows_per_group(const View &c, int rows, int splits, bool fused)
-{
-    const int nqt = rows_per_group(rows);
-    if (nqt != 2 || fused || c.preset != kPresetK8V4)
-        return nqt;
-    const long tiles = (c.max_seq + 31) / 32;
-    const long per_range = (tiles + splits - 1) / splits;
-    if (per_range > 2 * 8)
-        return nqt;
-    const long groups = (long)c.B * c.Hk * splits * row_tiles(rows);
-    return groups <= INT32_MAX ? 1 : nqt;
-}
-
 // Wavefronts of a 64-row work-group: four (one per SIMD, each taking a
-// quarter of the range's tiles, a four-state merge) when the key ranges are
-// short, eight (two per SIMD, an eight-state merge) otherwise.
+// quarter of the range's tiles; the merge of four 64-row states moves half
+// the LDS bytes of eight) when the key ranges are short, eight (two per
+// SIMD, which overlap each other's matrix-core and vector work) otherwise.
+// Measured at the PoC shape (16 ranges of 16 tiles, same box, graphs over
+// cold replicas): k8v4 verify 16.9 us with four against 17.9-18.7 with the
+// 32-row work-groups, fused k8v4 step 19.4 against 21.6 with eight, k4v4_nc
+// verify 18.0 against 18.5; k3v4_nc, whose key levels are byte-table
+// lookups (more vector instructions per tile, which a lone wavefront per
+// SIMD issues at half rate), 17.2 with eight against 18.2 with four, and at
+// long context (128-tile ranges) eight wavefronts are faster for every preset.
 int wide_waves(const View &c, int splits)
 {
     if (c.preset == kPresetK3V4)
@@ -374,7 +357,7 @@ int verify_impl(const View &v, const void *Knew, const void *Vnew, const void *Q
     a.btab = v.btab;
     a.bstride = v.bstride;
     a.npages = v.npages;
-    const int nqt = kernel_rows_per_group(v, R, splits, fused);
+    const int nqt = rows_per_group(R);
     if (launch_verify(v.preset, v.btab != nullptr, nqt, wide_waves(v, splits), R <= 8, a, s) != hipSuccess)
         return TQKV_ERR_LAUNCH;
     return TQKV_OK;

@@ -90,8 +90,8 @@ def summarise(t: np.ndarray, title: str) -> str:
     if n == 0:
         return "%s: no work-group of verify_wide_kernel ran (the call took the 32-row work-groups)" % title
     t = t[:n]
-    start = t[:, :, 0]
-    ws0 = start.min(axis=1)
+    start = np.where(t[:, :, 0] != 0, t[:, :, 0], np.iinfo(np.int64).max)
+    ws0 = start.min(axis=1)  # the work-group's first wavefront start (four-wavefront groups fill slots 0-3)
     rel = lambda v, s0: ((v - s0) % 2**32) / 100.0  # noqa: E731  100 MHz ticks -> us
     lines = ["%s: %d work-groups; us from each work-group's start, median over work-groups" % (title, n)]
     storing = t[:, 0, 20] == 1
@@ -100,6 +100,8 @@ def summarise(t: np.ndarray, title: str) -> str:
             continue
         lines.append("%s (%d):" % (name, int(m.sum())))
         for w in range(8):
+            if not (t[m][:, w, 0] != 0).any():
+                continue  # a work-group of four wavefronts
             row = []
             for k in ORDER:
                 v = t[m][:, w, k]
