@@ -1625,13 +1625,19 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
             return (p >= 0 && p < a.npages) ? a.wbase + ((size_t)p * a.Hk + hk) * L_::kBlockBytes : nullptr;
         }
     };
-    // Ring prefill: one tile per wavefront now (if it holds no new token),
-    // the rest once the query rows are prepared.  Loads issued here compete
-    // with the query loads for the memory system, and a wavefront whose
-    // load issue stalls (the memory pipeline full) holds up the work-group
-    // barriers of the query preparation; measured at the PoC shape 0.7 to
-    // 1.1 us per call faster than prefilling the whole ring here.
-    if (tq[0] < wt1 && (tq[0] + 1) * kTile <= tn0) {
+    // Ring prefill: a plain verify issues one tile per wavefront now, the
+    // rest from the first step; loads issued here compete with the query
+    // loads for the memory system, and a wavefront whose load issue stalls
+    // (the memory pipeline full) holds up the work-group barriers of the
+    // query preparation (measured at the PoC shape 0.7 to 1.1 us per call
+    // faster than prefilling the whole ring here).  A fused store + verify
+    // issues its first tile only once the query rows have landed: the
+    // work-groups that store the new tokens end last, and every load the
+    // others issue meanwhile competes with their token loads and stores
+    // (PoC step 18.6-19.2 against 19.3-20.0 us; the plain verify is 0.1-0.2
+    // us slower that way).
+    const bool early_tile = a.Knew == nullptr;
+    if (early_tile && tq[0] < wt1 && (tq[0] + 1) * kTile <= tn0) {
         issue(tq[0], ring_lds);
         ++issued;
     }
@@ -1692,6 +1698,10 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
         wait_vm<0>();
     TQKV_STAMP(1);
     lds_barrier();
+    if (!early_tile && issued == 0 && tq[0] < wt1) {
+        issue(tq[0], ring_lds);
+        ++issued;
+    }
 
     // 5. scale and round to binary16 (thread t: 16 coordinates of row
     //    t / 8, and with four wavefronts of row t / 8 + 32 as well); every
