@@ -1960,8 +1960,12 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
         ValRegs vr;
         read_values<PRESET>(vr, slot, lane);
         if constexpr (MASKED) {
-            // fields of tokens past the sequence end never enter (they may hold anything)
+            // fields of tokens past the sequence end never enter (they may
+            // hold anything); the zeros, which the row sums' A operand shares
+            // between rows that see a token and rows that do not, are clamped
+            // to the finite range (below: P * vscale per row)
             const int lim = L - tok0 - 8 * h;
+            const half2_t big = half2_t{(_Float16)65504.0f, (_Float16)65504.0f};
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -1969,7 +1973,10 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
                     const uint32_t keep = ((16 * s2 + 2 * j < lim) ? 0x0000FFFFu : 0u) |
                                           ((16 * s2 + 2 * j + 1 < lim) ? 0xFFFF0000u : 0u);
                     vr.vs[s2][j] &= keep;
-                    vr.vz[s2][j] &= keep;
+                    const uint32_t z = vr.vz[s2][j] & keep;
+                    vr.vz[s2][j] = __builtin_bit_cast(
+                        uint32_t,
+                        __builtin_elementwise_min(__builtin_elementwise_max(__builtin_bit_cast(half2_t, z), -big), big));
                 }
         }
 #pragma unroll
@@ -1989,6 +1996,16 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
                     Pr.u[j] = __builtin_bit_cast(uint32_t, ph);
                     As.u[j] = sum_zlane[qt] ? vzj : sum_ones[qt];
                     Bp.u[j] = __builtin_bit_cast(uint32_t, ph * __builtin_bit_cast(half2_t, vsj));
+                    if constexpr (MASKED) {
+                        // masked tiles hold tokens that some rows do not see
+                        // (P = 0): P * vscale is kept only where P is not 0,
+                        // so that an infinite value scale (values with an
+                        // infinity) reaches exactly the rows that see its token
+                        // (0 * inf would be NaN); the zeros of the row sums'
+                        // A operand, shared by all rows, were clamped above
+                        const uint32_t pu = __builtin_bit_cast(uint32_t, ph);
+                        Bp.u[j] &= ((pu & 0x00007FFFu) ? 0x0000FFFFu : 0u) | ((pu & 0x7FFF0000u) ? 0xFFFF0000u : 0u);
+                    }
                 }
                 sums = __builtin_amdgcn_mfma_f32_32x32x16_f16(As.h, Pr.h, sums, 0, 0, 0);
 #pragma unroll

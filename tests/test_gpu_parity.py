@@ -342,6 +342,24 @@ def test_verify_nan_parity(preset):
 
 
 @pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
+@pytest.mark.parametrize("Hq", [2, 8], ids=["rows16", "rows64"])
+@pytest.mark.parametrize("val", [np.inf, -np.inf], ids=["inf", "neg_inf"])
+def test_verify_infinite_value_parity(preset, Hq, val):
+    """An infinite value element makes its token's value scale infinite (and,
+    for -inf, its zero): exactly the rows that can see the token turn NaN,
+    in the 32-row work-groups (16 rows) and the 64-row ones alike."""
+    cfg = _small(preset, B=1, Hk=1, Hq=Hq, N=8, S=64)
+    inp = synth.make_inputs(cfg)
+    inp["V"][0, 60, 0, 5] = np.float16(val)  # position 60: row n sees 57 + n tokens
+    ocache = _oracle_cache(cfg, inp)
+    ref = oracle.verify(preset, ocache, 1, 1, 64, inp["Q"], inp["seq_lens"], Hq, True)
+    assert np.isnan(ref[4:]).all() and np.isfinite(ref[:4]).all()
+    cache = gpu_store_all(cfg, inp)
+    for ns in (1, 3):
+        assert_close(_gpu_verify(cache, cfg, inp, num_splits=ns), ref, what="infinite value splits=%d" % ns)
+
+
+@pytest.mark.parametrize("preset", PRESETS, ids=PNAME.get)
 def test_verify_causality_and_determinism(preset):
     cfg = _small(preset)
     inp = synth.make_inputs(cfg)
