@@ -137,6 +137,7 @@ template <int NQT> struct Ring<kPresetK8V4, NQT> {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 // s_waitcnt vmcnt(N) with a compile-time N; the memory clobber keeps the
 // compiler from moving LDS reads of the waited-for slot above it.
@@ -145,6 +146,13 @@ template <int N> __device__ inline void wait_vm()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ inline void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) that the compiler sees (the waits above are opaque to
+// it): after it, the compiler takes every memory instruction it issued
+// itself as complete.  It counts only its own loads and stores, not the
+// ring's DMA (inline asm), so wherever it believes one of its own may still
+// be in flight it waits with vmcnt(0), which in hardware also waits for
+// every ring tile in flight.
+__device__ inline void wait_vm0_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // wait until at most `tiles` ring tiles (of LPT instructions each) are in
 // flight; counts above 8 tiles are never needed (depth <= 8)
@@ -643,38 +651,10 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
 
     // ------------------------------------------------------------ prologue
-    // 0. fused store: the new tokens [tn0, L) of this unit that fall in this
-    //    work-group's key range; this wavefront's first two token-heads are
-    //    loaded now, so their memory latency overlaps the query and ring loads
+    // the fused store's new tokens [tn0, L) of this unit that fall in this
+    // work-group's key range
     const int tn0 = (a.Knew != nullptr) ? L - nq : L;
     const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile); // this work-group's share
-    quant::TokenHead nx1{0, 0, 0, 0}, nx2{0, 0, 0, 0};
-    if (wn0 + wave < wn1) {
-        const int t = wn0 + wave, t2 = min(t + kWaves, wn1 - 1);
-        const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
-        const size_t src2 = ((size_t)(qt0 + (t2 - tn0) * qts) * a.Hk + hk) * kD;
-        nx1 = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
-        nx2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
-    }
-
-    // 1. The unit's raw query rows -> LDS, 1 KiB per load (2 fp32 or 4 fp16
-    //    rows).  Padding rows re-read row 0 and are zeroed below.  Every
-    //    wavefront queues these loads before any wavefront queues ring loads,
-    //    so the query does not wait behind the key stream.
-    {
-        const int esz = a.q_f16 ? 2 : 4;
-        const int rshift = a.q_f16 ? 4 : 5; // lanes per row: 16 or 32
-        const int rpi = 64 >> rshift;       // rows per load
-        const int rsub = lane >> rshift, cb = 16 * (lane & ((1 << rshift) - 1));
-        for (int J = wave; J < RP / rpi; J += kWaves) {
-            const int r = row0 + J * rpi + rsub;
-            const int rs = r < Rb ? r : 0;
-            const int n = row_token(rs), g = rs - n * a.G;
-            const uint8_t *src = static_cast<const uint8_t *>(a.Q) +
-                                 ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD * esz + cb;
-            dma16(src, lds0 + 1024 * J);
-        }
-    }
     // paged cache: the page ids of this wavefront's blocks 2 kt0 + [0, 128)
     // (lane l of pidv[c]: block 2 kt0 + 64 c + l; the launch plan keeps a
     // wavefront at no more than 64 tiles).  Ids outside the pool read page
@@ -682,15 +662,6 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     const int nbl = (L + kBlockTokens - 1) / kBlockTokens; // blocks holding tokens
     const int32_t *brow = PAGED ? a.btab + (size_t)b * a.bstride : nullptr;
     int pidv[2] = {0, 0};
-    if constexpr (PAGED) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int j = 2 * kt0 + 64 * c + lane;
-            const int p = (j < nbl) ? brow[j] : 0;
-            pidv[c] = (p >= 0 && p < a.npages) ? p : 0;
-        }
-    }
-    __builtin_amdgcn_s_barrier();
 
     // 2. the first ring tiles.  The ring fills progressively (at most two
     //    tiles per step): a load instruction waits at issue while the memory
@@ -731,8 +702,38 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     // tiles holding new tokens are loaded only after they have been stored
     // (step 3)
     const int pre = min(kInitTiles, max(0, min(ntile, (tn0 - kt0 * kTile) / kTile)));
-    for (; issued < pre; ++issued)
-        issue(issued, ring_lds + issued * kSlotBytes);
+    // 1. the query rows, the page ids and the first ring tiles
+    auto start_loads = [&]() {
+        // the unit's raw query rows -> LDS, 1 KiB per load (2 fp32 or 4
+        // fp16 rows).  Padding rows re-read row 0 and are zeroed below.
+        // Every wavefront queues these loads before any wavefront queues
+        // ring loads, so the query does not wait behind the key stream.
+        {
+            const int esz = a.q_f16 ? 2 : 4;
+            const int rshift = a.q_f16 ? 4 : 5; // lanes per row: 16 or 32
+            const int rpi = 64 >> rshift;       // rows per load
+            const int rsub = lane >> rshift, cb = 16 * (lane & ((1 << rshift) - 1));
+            for (int J = wave; J < RP / rpi; J += kWaves) {
+                const int r = row0 + J * rpi + rsub;
+                const int rs = r < Rb ? r : 0;
+                const int n = row_token(rs), g = rs - n * a.G;
+                const uint8_t *src = static_cast<const uint8_t *>(a.Q) +
+                                     ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD * esz + cb;
+                dma16(src, lds0 + 1024 * J);
+            }
+        }
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int j = 2 * kt0 + 64 * c + lane;
+                const int p = (j < nbl) ? brow[j] : 0;
+                pidv[c] = (p >= 0 && p < a.npages) ? p : 0;
+            }
+        }
+        __builtin_amdgcn_s_barrier();
+        for (; issued < pre; ++issued)
+            issue(issued, ring_lds + issued * kSlotBytes);
+    };
 
     // 3. Fused store: the work-group whose key range holds new tokens of
     //    this unit quantises them into the cache first (the bytes tqkv_store
@@ -740,7 +741,21 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
     //    stores are complete before any wavefront loads a tile that holds
     //    them.  (Work-groups of the other row tiles store the same tokens
     //    again: identical bytes.)
+    //    This wavefront's first two token-heads are loaded before the
+    //    query rows, so their memory latency overlaps the query and ring
+    //    loads.  The loads and the stores are all in this branch, which
+    //    ends in a wait the compiler sees: no path past it leaves one in
+    //    its books (it would wait for the query and ring loads too).
     if (wn0 < wn1) {
+        quant::TokenHead nx1{0, 0, 0, 0}, nx2{0, 0, 0, 0};
+        if (wn0 + wave < wn1) {
+            const int t = wn0 + wave, t2 = min(t + kWaves, wn1 - 1);
+            const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+            const size_t src2 = ((size_t)(qt0 + (t2 - tn0) * qts) * a.Hk + hk) * kD;
+            nx1 = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+            nx2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+        }
+        start_loads();
         // two token-heads per wavefront at a time, both loaded up front (the
         // first two at the kernel start)
         for (int t = wn0 + wave; t < wn1; t += 2 * kWaves) {
@@ -778,6 +793,8 @@ __global__ __launch_bounds__(256, NQT == 1 ? 2 : 1) void verify_kernel(VerifyArg
         // reusing those registers)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    } else {
+        start_loads();
     }
     for (; issued < min(kInitTiles, ntile); ++issued)
         issue(issued, ring_lds + issued * kSlotBytes);
@@ -1558,21 +1575,17 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
     _Float16 *qs = reinterpret_cast<_Float16 *>(lds);
 
     // ------------------------------------------------------------ prologue
-    // 0. fused store: this wavefront's first new token-head(s) are loaded
-    //    now, so their memory latency overlaps the query and ring loads
     const int tn0 = (a.Knew != nullptr) ? L - nq : L;
     const int wn0 = max(tn0, wt0 * kTile), wn1 = min(L, wt1 * kTile);
-    quant::TokenHead nx1{0, 0, 0, 0}, nx2{0, 0, 0, 0};
-    if (wn0 + wave < wn1) {
-        const int t = wn0 + wave, t2 = min(t + kW, wn1 - 1);
-        const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
-        const size_t src2 = ((size_t)(qt0 + (t2 - tn0) * qts) * a.Hk + hk) * kD;
-        nx1 = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
-        nx2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
-    }
-
-    // 1. raw query rows -> LDS, queued before any ring load
-    {
+    const int nbl = (L + kBlockTokens - 1) / kBlockTokens;
+    const int32_t *brow = PAGED ? a.btab + (size_t)b * a.bstride : nullptr;
+    // the same row for the ring's page ids, read through the scalar cache: a
+    // vector load there would make the compiler wait for it with vmcnt(0),
+    // i.e. for every ring tile in flight (the table is not written during
+    // the launch)
+    const const_i32_t *brow_s = (const const_i32_t *)(uintptr_t)brow;
+    // 1. raw query rows -> LDS, every wavefront's queued before any ring load
+    auto load_query = [&]() {
         const int esz = a.q_f16 ? 2 : 4;
         const int rshift = a.q_f16 ? 4 : 5;
         const int rpi = 64 >> rshift;
@@ -1585,10 +1598,8 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
                                  ((size_t)(qt0 + n * qts) * a.Hq + hk * a.G + g) * kD * esz + cb;
             dma16(src, lds0 + 1024 * J);
         }
-    }
-    const int nbl = (L + kBlockTokens - 1) / kBlockTokens;
-    const int32_t *brow = PAGED ? a.btab + (size_t)b * a.bstride : nullptr;
-    __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_s_barrier();
+    };
 
     // 2. the first ring tiles
     const uint32_t voff = 16 * lane;
@@ -1603,7 +1614,7 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
             // of range read page 0, whose tokens the mask never admits)
             const int j = 2 * t;
             const bool two = j + 1 < nbl;
-            int p0 = brow[j], p1 = two ? brow[j + 1] : 0;
+            int p0 = brow_s[j], p1 = two ? brow_s[j + 1] : 0;
             p0 = (p0 >= 0 && p0 < a.npages) ? p0 : 0;
             p1 = (p1 >= 0 && p1 < a.npages) ? p1 : 0;
             const uint8_t *src0 = a.base + ((size_t)p0 * a.Hk + hk) * L_::kBlockBytes;
@@ -1637,16 +1648,24 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
     // (PoC step 18.6-19.2 against 19.3-20.0 us; the plain verify is 0.1-0.2
     // us slower that way).
     const bool early_tile = a.Knew == nullptr;
-    if (early_tile && tq[0] < wt1 && (tq[0] + 1) * kTile <= tn0) {
-        issue(tq[0], ring_lds);
-        ++issued;
-    }
-
     // 3. fused store of this work-group's share of the new tokens, spread
-    //    over the eight wavefronts; complete (the wait for the query rows
-    //    below) before any tile holding them is loaded
+    //    over the wavefronts; complete (the wait for the query rows
+    //    below) before any tile holding them is loaded.  Its loads and
+    //    stores end in a wait the compiler sees, so that it does not wait
+    //    for them (and so for the ring) again in the query preparation
     TQKV_SET(20, wn0 < wn1 ? 1u : 0u);
     if (wn0 < wn1) {
+        // this wavefront's first new token-head(s), loaded before the
+        // query rows so that their latency overlaps the query loads
+        quant::TokenHead nx1{0, 0, 0, 0}, nx2{0, 0, 0, 0};
+        if (wn0 + wave < wn1) {
+            const int t = wn0 + wave, t2 = min(t + kW, wn1 - 1);
+            const size_t src = ((size_t)(qt0 + (t - tn0) * qts) * a.Hk + hk) * kD;
+            const size_t src2 = ((size_t)(qt0 + (t2 - tn0) * qts) * a.Hk + hk) * kD;
+            nx1 = quant::load_token_head(a.Knew + src, a.Vnew + src, lane);
+            nx2 = quant::load_token_head(a.Knew + src2, a.Vnew + src2, lane);
+        }
+        load_query();
         TQKV_STAMP(16);
         for (int t = wn0 + wave; t < wn1; t += 2 * kW) {
             const int t2 = t + kW;
@@ -1674,6 +1693,13 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
             }
         }
         TQKV_STAMP(17);
+        wait_vm0_known(); // the query rows are waited for next anyway
+    } else {
+        load_query();
+        if (early_tile && tq[0] < wt1 && (tq[0] + 1) * kTile <= tn0) {
+            issue(tq[0], ring_lds);
+            ++issued;
+        }
     }
     // 4. state
     int erow[NQT];
@@ -1690,12 +1716,10 @@ __global__ __launch_bounds__(64 * kW, 1) void verify_wide_kernel(VerifyArgs a)
     uint32_t *claim_ctr = reinterpret_cast<uint32_t *>(lds + kQRegion - 16);
     static_assert(RP * kQStride * 2 <= kQRegion - 16, "claim counter");
 
-    // this wavefront's query loads have landed; a wavefront that stored new
-    // tokens waits for its stores too, so after the barrier every new token
-    // is in memory (the ring loads of tiles that hold them come later)
+    // this wavefront's query loads have landed (a wavefront that stored new
+    // tokens has waited for its stores too, so after the barrier every new
+    // token is in memory; the ring loads of tiles that hold them come later)
     wait_ring<LPT>(issued);
-    if (wn0 + wave < wn1)
-        wait_vm<0>();
     TQKV_STAMP(1);
     lds_barrier();
     if (!early_tile && issued == 0 && tq[0] < wt1) {
