@@ -161,8 +161,10 @@ int rows_per_group(int rows) { return row_tiles(rows) >= 2 ? 2 : 1; }
 // 32-row work-groups, fused k8v4 step 19.4 against 21.6 with eight, k4v4_nc
 // verify 18.0 against 18.5; k3v4_nc, whose key levels are byte-table
 // lookups (more vector instructions per tile, which a lone wavefront per
-// SIMD issues at half rate), 17.2 with eight against 18.2 with four, and at
-// long context (128-tile ranges) eight wavefronts are faster for every preset.
+// SIMD issues at half rate), 17.2 with eight against 18.2 with four (16.0-16.2
+// against 16.7 once the query preparation no longer waited for the ring),
+// and at long context (128-tile ranges) eight wavefronts are faster for every
+// preset.
 int wide_waves(const View &c, int splits)
 {
     if (c.preset == kPresetK3V4)
